@@ -1,0 +1,279 @@
+"""Python binding of libmoe (MI355X / gfx950 MoE-layer hot path).
+
+A thin ctypes layer over the C ABI in ``include/moe.h``: it checks tensor
+shapes and dtypes, passes ``data_ptr()`` and the current HIP stream, and turns
+status codes into exceptions.  Every step of the layer runs in the library's
+HIP kernels; there is no fallback.  If ``libmoe.so`` has not been built, every
+call raises.
+
+Functions (same names as the C calls):
+    route(p, x, w_gate, bias=None, want_logits=False) -> (topk_idx, topk_w[, logits])
+    dispatch(p, topk_idx, x) -> dict(counts_all, offsets, perm, inv, x_packed)
+    expert_gemm(p, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
+    combine(p, y_packed, inv, topk_w) -> y
+    layer(p, x, w_gate, bias, w1, w3, w2, routing=False, overlap=False, ...) -> y or (y, dict)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_F_WRITE_LOGITS, MOE_F_OVERLAP = 1, 2
+MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_EXPERT_GEMM, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
+
+EXPORTED = ["moe_last_error", "moe_version", "moe_workspace_bytes", "moe_route", "moe_dispatch",
+            "moe_expert_gemm", "moe_combine", "moe_layer"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libmoe status {status}: {msg}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("f", ctypes.c_int32), ("expert_lo", ctypes.c_int32),
+                ("n_local", ctypes.c_int32), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class RoutingOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "logits", "counts_all", "offsets", "perm", "inv")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built; run python -m combine_router_top_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        P = ctypes.POINTER(Problem)
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_version.restype = ctypes.c_char_p
+        L.moe_workspace_bytes.argtypes = [P, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_gemm.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
+        L.moe_layer.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(RoutingOut), vp, sz,
+                                vp, vp]
+        for n in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_layer"):
+            getattr(L, n).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(st: int):
+    if st != MOE_OK:
+        raise MoeError(st, lib().moe_last_error().decode())
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Problem description (mirrors moe_problem_t)."""
+    T: int
+    d: int
+    E: int
+    k: int
+    f: int
+    expert_lo: int
+    n_local: int
+    dtype: str  # "bf16" or "f32"
+    flags: int = 0
+
+    @property
+    def rows_max(self) -> int:
+        return self.T * min(self.k, self.n_local)
+
+    def c(self) -> Problem:
+        return Problem(self.T, self.d, self.E, self.k, self.f, self.expert_lo, self.n_local,
+                       MOE_DTYPE_BF16 if self.dtype == "bf16" else MOE_DTYPE_F32, self.flags)
+
+    @staticmethod
+    def of(w, flags: int = 0) -> "Spec":
+        """From any object with T, d, E, k, f, expert_lo, n_local, dtype fields."""
+        return Spec(w.T, w.d, w.E, w.k, w.f, w.expert_lo, w.n_local, w.dtype, flags)
+
+
+def workspace_bytes(p: Spec, call: int = MOE_CALL_LAYER) -> int:
+    pc = p.c()
+    n = lib().moe_workspace_bytes(ctypes.byref(pc), call)
+    if n == 0 and lib().moe_last_error():
+        raise MoeError(MOE_ERR_INVALID_ARG, lib().moe_last_error().decode())
+    return int(n)
+
+
+# ---------------------------------------------------------------------------
+# torch helpers (device memory and streams only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(p: Spec):
+    t = _torch()
+    return t.bfloat16 if p.dtype == "bf16" else t.float32
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    t = _torch()
+    s = stream if stream is not None else t.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t, shape, dtype, name):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t
+
+
+def alloc_workspace(p: Spec, call: int = MOE_CALL_LAYER, device="cuda"):
+    torch = _torch()
+    n = workspace_bytes(p, call)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device) if n else None
+
+
+# ---------------------------------------------------------------------------
+# the five calls
+# ---------------------------------------------------------------------------
+def route(p: Spec, x, w_gate, bias=None, want_logits: bool = False, workspace=None, stream=None,
+          out=None):
+    torch = _torch()
+    dt = _dt(p)
+    _need(x, (p.T, p.d), dt, "x")
+    _need(w_gate, (p.d, p.E), dt, "w_gate")
+    if bias is not None:
+        _need(bias, (p.E,), torch.float32, "bias")
+    dev = x.device
+    idx = torch.empty((p.T, p.k), dtype=torch.int32, device=dev) if out is None else out[0]
+    w = torch.empty((p.T, p.k), dtype=torch.float32, device=dev) if out is None else out[1]
+    logits = torch.empty((p.T, p.E), dtype=torch.float32, device=dev) if want_logits else None
+    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_ROUTE, dev)
+    pc = p.c()
+    _check(lib().moe_route(ctypes.byref(pc), _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(logits),
+                           _ptr(idx), _ptr(w), _ptr(ws), 0 if ws is None else ws.numel(),
+                           _stream(stream)))
+    return (idx, w, logits) if want_logits else (idx, w)
+
+
+def dispatch(p: Spec, topk_idx, x, workspace=None, stream=None) -> Dict[str, object]:
+    torch = _torch()
+    dt = _dt(p)
+    _need(topk_idx, (p.T, p.k), torch.int32, "topk_idx")
+    _need(x, (p.T, p.d), dt, "x")
+    dev = x.device
+    o = {
+        "counts_all": torch.empty(p.E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(p.n_local + 1, dtype=torch.int32, device=dev),
+        "perm": torch.full((p.rows_max,), -7, dtype=torch.int32, device=dev),
+        "inv": torch.empty(p.T * p.k, dtype=torch.int32, device=dev),
+        "x_packed": torch.zeros((p.rows_max, p.d), dtype=dt, device=dev),
+    }
+    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_DISPATCH, dev)
+    pc = p.c()
+    _check(lib().moe_dispatch(ctypes.byref(pc), _ptr(topk_idx), _ptr(x), _ptr(o["counts_all"]),
+                              _ptr(o["offsets"]), _ptr(o["perm"]), _ptr(o["inv"]),
+                              _ptr(o["x_packed"]), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(stream)))
+    return o
+
+
+def expert_gemm(p: Spec, x_packed, offsets, w1, w3, w2, workspace=None, stream=None, out=None):
+    torch = _torch()
+    dt = _dt(p)
+    _need(x_packed, (p.rows_max, p.d), dt, "x_packed")
+    _need(offsets, (p.n_local + 1,), torch.int32, "offsets")
+    _need(w1, (p.n_local, p.d, p.f), dt, "w1")
+    _need(w3, (p.n_local, p.d, p.f), dt, "w3")
+    _need(w2, (p.n_local, p.f, p.d), dt, "w2")
+    dev = x_packed.device
+    if out is None:
+        h = torch.zeros((p.rows_max, p.f), dtype=dt, device=dev)
+        yp = torch.zeros((p.rows_max, p.d), dtype=dt, device=dev)
+    else:
+        h, yp = out
+    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_EXPERT_GEMM, dev)
+    pc = p.c()
+    _check(lib().moe_expert_gemm(ctypes.byref(pc), _ptr(x_packed), _ptr(offsets), _ptr(w1),
+                                 _ptr(w3), _ptr(w2), _ptr(h), _ptr(yp), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)))
+    return h, yp
+
+
+def combine(p: Spec, y_packed, inv, topk_w, stream=None, out=None):
+    torch = _torch()
+    dt = _dt(p)
+    _need(y_packed, (p.rows_max, p.d), dt, "y_packed")
+    _need(inv, (p.T * p.k,), torch.int32, "inv")
+    _need(topk_w, (p.T, p.k), torch.float32, "topk_w")
+    y = torch.empty((p.T, p.d), dtype=dt, device=y_packed.device) if out is None else out
+    pc = p.c()
+    _check(lib().moe_combine(ctypes.byref(pc), _ptr(y_packed), _ptr(inv), _ptr(topk_w), _ptr(y),
+                             _stream(stream)))
+    return y
+
+
+def layer(p: Spec, x, w_gate, bias, w1, w3, w2, routing: bool = False, want_logits: bool = False,
+          overlap: bool = False, workspace=None, stream=None, stream2=None, out=None):
+    """The whole layer.  With ``routing`` also returns the routing/dispatch
+    tensors; with ``overlap`` runs the two-stream dispatch overlap (needs
+    ``stream2``, a torch.cuda.Stream, or creates none and runs one stream)."""
+    torch = _torch()
+    dt = _dt(p)
+    _need(x, (p.T, p.d), dt, "x")
+    _need(w_gate, (p.d, p.E), dt, "w_gate")
+    if bias is not None:
+        _need(bias, (p.E,), torch.float32, "bias")
+    _need(w1, (p.n_local, p.d, p.f), dt, "w1")
+    _need(w3, (p.n_local, p.d, p.f), dt, "w3")
+    _need(w2, (p.n_local, p.f, p.d), dt, "w2")
+    dev = x.device
+    flags = p.flags | (MOE_F_WRITE_LOGITS if want_logits else 0) | (MOE_F_OVERLAP if overlap else 0)
+    q = Spec(p.T, p.d, p.E, p.k, p.f, p.expert_lo, p.n_local, p.dtype, flags)
+    y = torch.empty((p.T, p.d), dtype=dt, device=dev) if out is None else out
+    r = None
+    ro = None
+    if routing or want_logits:
+        r = {
+            "topk_idx": torch.empty((p.T, p.k), dtype=torch.int32, device=dev),
+            "topk_w": torch.empty((p.T, p.k), dtype=torch.float32, device=dev),
+            "counts_all": torch.empty(p.E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(p.n_local + 1, dtype=torch.int32, device=dev),
+            "perm": torch.full((p.rows_max,), -7, dtype=torch.int32, device=dev),
+            "inv": torch.empty(p.T * p.k, dtype=torch.int32, device=dev),
+        }
+        if want_logits:
+            r["logits"] = torch.empty((p.T, p.E), dtype=torch.float32, device=dev)
+        ro = RoutingOut(*[_ptr(r.get(n)) for n in
+                          ("topk_idx", "topk_w", "logits", "counts_all", "offsets", "perm", "inv")])
+    ws = workspace if workspace is not None else alloc_workspace(q, MOE_CALL_LAYER, dev)
+    pc = q.c()
+    s2 = _stream(stream2) if (overlap and stream2 is not None) else None
+    _check(lib().moe_layer(ctypes.byref(pc), _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(w1), _ptr(w3),
+                           _ptr(w2), _ptr(y), ctypes.byref(ro) if ro is not None else None,
+                           _ptr(ws), ws.numel(), _stream(stream), s2))
+    return (y, r) if r is not None else y

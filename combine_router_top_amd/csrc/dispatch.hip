@@ -1,0 +1,237 @@
+// Dispatch: per-expert histogram, prefix scan and stable permutation of the
+// local (token, slot) assignments into expert-contiguous, unpadded segments,
+// then the row gather x_packed[p] = x[perm[p] / k].  This is the one-GPU
+// share of the pages' MoE dispatch with variable-size per-peer transfers and
+// no padding ("CUCo: An Agentic Framework for Compute and Communication
+// Co-design", Table 4, row "MoE Dispatch/Combine").
+//
+// The permutation is a stable counting sort computed without global atomics,
+// so it is bitwise deterministic:
+//   chunk_hist_kernel  one workgroup per chunk of 1024 assignments: LDS
+//                      histogram over all E experts (integer atomics in LDS
+//                      are order-free).
+//   scatter_kernel     one workgroup per chunk: reads every chunk's histogram
+//                      (a few KB), forms the global counts, the exclusive scan
+//                      over local experts (offsets) and this chunk's base per
+//                      expert, then ranks its assignments stably: four waves
+//                      of 256 consecutive assignments each, wave-to-wave
+//                      prefix in LDS, and inside a wave the rank among equal
+//                      experts from ballots over the expert-id bits.
+//   gather_rows_kernel one wave per packed row, 16-byte vector copies.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int DCH = 1024;   // assignments per chunk
+constexpr int DMAXE = 1024; // max experts
+
+__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ idx,
+                                                         int64_t TK, int E,
+                                                         int32_t* __restrict__ chunk_hist) {
+  __shared__ int h[DMAXE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * DCH;
+#pragma unroll
+  for (int q = 0; q < DCH / 256; ++q) {
+    const int64_t a = base + q * 256 + tid;
+    if (a < TK) {
+      const int e = idx[a];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) chunk_hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Exclusive scan over 256 threads; returns this thread's prefix, total in *tot.
+__device__ __forceinline__ int block_excl_scan_256(int v, int* lds4, int* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) lds4[wave] = x;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += lds4[w];
+  *tot = lds4[0] + lds4[1] + lds4[2] + lds4[3];
+  __syncthreads();
+  return wbase + x - v;
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, int64_t TK,
+                                                      int E, int lo, int n, int nchunks,
+                                                      const int32_t* __restrict__ chunk_hist,
+                                                      int32_t* __restrict__ counts_all,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ inv) {
+  __shared__ int base[DMAXE];
+  __shared__ int wpos[4][DMAXE];
+  __shared__ int scan_tmp[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+
+  // 1. per local expert: total count and count in the chunks before this one
+  for (int e = tid; e < n; e += 256) {
+    int tot = 0, pre = 0;
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int v = chunk_hist[(int64_t)cc * E + lo + e];
+      pre += cc < c ? v : 0;
+      tot += v;
+    }
+    base[e] = tot;
+    wpos[0][e] = pre;
+  }
+  __syncthreads();
+
+  // 2. exclusive scan of the local totals: thread t owns experts 4t .. 4t+3
+  int v4[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * tid + q;
+    v4[q] = e < n ? base[e] : 0;
+    s += v4[q];
+  }
+  int total;
+  int run = block_excl_scan_256(s, scan_tmp, &total);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * tid + q;
+    if (e < n) {
+      if (c == 0) offsets[e] = run;
+      base[e] = run + wpos[0][e];
+    }
+    run += v4[q];
+  }
+  if (c == 0) {
+    if (tid == 0) offsets[n] = total;
+    for (int e = tid; e < E; e += 256) {
+      int t = 0;
+      for (int cc = 0; cc < nchunks; ++cc) t += chunk_hist[(int64_t)cc * E + e];
+      counts_all[e] = t;
+    }
+  }
+  __syncthreads();
+
+  // 3. per-wave counts of local experts over the wave's 256 assignments
+  for (int e = lane; e < n; e += 64) wpos[wave][e] = 0;
+  __syncthreads();
+  const int64_t wbeg = (int64_t)c * DCH + wave * 256;
+  int key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t a = wbeg + r * 64 + lane;
+    int e = -1;
+    if (a < TK) {
+      e = idx[a] - lo;
+      if ((unsigned)e >= (unsigned)n) e = -1;
+    }
+    key[r] = e;
+    if (e >= 0) atomicAdd(&wpos[wave][e], 1);
+  }
+  __syncthreads();
+
+  // 4. turn the per-wave counts into per-wave starting positions
+  for (int e = tid; e < n; e += 256) {
+    int p = base[e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t = wpos[w][e];
+      wpos[w][e] = p;
+      p += t;
+    }
+  }
+  __syncthreads();
+
+  // 5. stable ranks inside each wave, rounds in assignment order
+  const int nbits = n > 1 ? 32 - __clz(n - 1) : 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t a = wbeg + r * 64 + lane;
+    const int e = key[r];
+    const bool valid = e >= 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    int pos = -1;
+    if (valid) {
+      const int rank = __popcll(peers & lanemask_lt());
+      pos = wpos[wave][e] + rank;
+    }
+    // all lanes have read their position before the leaders advance the counters
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & lanemask_lt()) == 0) wpos[wave][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (a < TK) {
+      inv[a] = pos;
+      if (valid) perm[pos] = (int32_t)a;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ x,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ perm,
+                                                          u32x4* __restrict__ xp, int nvec, int k,
+                                                          int e_begin, int e_end) {
+  const int lane = threadIdx.x & 63;
+  const int64_t p = (int64_t)offsets[e_begin] + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= offsets[e_end]) return;
+  const int t = perm[p] / k;
+  const u32x4* src = x + (int64_t)t * nvec;
+  u32x4* dst = xp + p * nvec;
+  for (int v0 = lane; v0 < nvec; v0 += 256) {
+    u32x4 buf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + 64 * u;
+      if (v < nvec) buf[u] = src[v];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + 64 * u;
+      if (v < nvec) dst[v] = buf[u];
+    }
+  }
+}
+
+static int64_t n_chunks(const Prob& p) { return (p.tk() + DCH - 1) / DCH; }
+
+size_t dispatch_ws_bytes(const Prob& p) { return (size_t)n_chunks(p) * p.E * sizeof(int32_t); }
+
+hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                                 hipStream_t st) {
+  int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws);
+  const int64_t nc = n_chunks(p);
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
+                     chunk_hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E, p.lo,
+                     p.n, (int)nc, chunk_hist, counts_all, offsets, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const Prob& p, const void* x, const int32_t* offsets,
+                         const int32_t* perm, void* x_packed, int e_begin, int e_end,
+                         hipStream_t st) {
+  const int nvec = (int)((int64_t)p.d * p.elem() / 16);
+  const int64_t rows = p.rows_max;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 3) / 4));
+  hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, st, (const u32x4*)x, offsets, perm,
+                     (u32x4*)x_packed, nvec, p.k, e_begin, e_end);
+  return hipGetLastError();
+}
+
+}  // namespace moe

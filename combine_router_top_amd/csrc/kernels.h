@@ -1,0 +1,36 @@
+// Internal launchers of libmoe (host functions defined next to their kernels).
+// All take a validated problem and launch asynchronously on `st`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace moe {
+
+// route.hip
+size_t route_ws_bytes(const Prob& p);
+hipError_t launch_route(const Prob& p, const void* x, const void* wg, const float* bias,
+                        float* logits, int32_t* idx, float* w, void* ws, hipStream_t st);
+
+// dispatch.hip
+size_t dispatch_ws_bytes(const Prob& p);
+hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                                 hipStream_t st);
+// Gather rows of the local experts [e_begin, e_end) (0-based local indices).
+hipError_t launch_gather(const Prob& p, const void* x, const int32_t* offsets,
+                         const int32_t* perm, void* x_packed, int e_begin, int e_end,
+                         hipStream_t st);
+
+// expert_gemm.hip: GEMMs over the segments of local experts [e_begin, e_end)
+size_t expert_gemm_ws_bytes(const Prob& p);
+hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
+                              const void* w1, const void* w3, const void* w2, void* h,
+                              void* y_packed, void* ws, int e_begin, int e_end, hipStream_t st);
+
+// combine.hip
+hipError_t launch_combine(const Prob& p, const void* y_packed, const int32_t* inv,
+                          const float* w, void* y, hipStream_t st);
+
+}  // namespace moe

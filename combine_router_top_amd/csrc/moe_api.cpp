@@ -1,0 +1,334 @@
+// C ABI of libmoe: argument validation, workspace layout and launch order.
+// Validation is shape-only and runs before any HIP call, so invalid calls are
+// rejected (and testable) on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status_t ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status_t check_problem(const moe_problem_t* p, moe::Prob* out) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
+  if (p->T <= 0 || p->d <= 0 || p->E <= 0 || p->k <= 0 || p->f <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "T, d, E, k, f must be positive (T=%d d=%d E=%d k=%d f=%d)",
+                p->T, p->d, p->E, p->k, p->f);
+  if (p->k > p->E) return fail(MOE_ERR_INVALID_ARG, "k=%d exceeds E=%d", p->k, p->E);
+  if (p->n_local <= 0 || p->expert_lo < 0 || (int64_t)p->expert_lo + p->n_local > p->E)
+    return fail(MOE_ERR_INVALID_ARG, "local experts [%d, %d+%d) not inside [0, %d)", p->expert_lo,
+                p->expert_lo, p->n_local, p->E);
+  if (p->flags & ~(uint32_t)(MOE_F_WRITE_LOGITS | MOE_F_OVERLAP))
+    return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+  if (p->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k=%d > 32 not supported", p->k);
+  if (p->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E=%d > 1024 not supported", p->E);
+  if (p->d % 8 != 0 || p->f % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "d=%d and f=%d must be multiples of 8", p->d, p->f);
+  const int64_t tk = (int64_t)p->T * p->k;
+  if (tk >= (int64_t)1 << 30)
+    return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld too large", (long long)tk);
+  moe::Prob q;
+  q.T = p->T;
+  q.d = p->d;
+  q.E = p->E;
+  q.k = p->k;
+  q.f = p->f;
+  q.lo = p->expert_lo;
+  q.n = p->n_local;
+  q.dtype = p->dtype;
+  q.flags = p->flags;
+  q.rows_max = (int64_t)p->T * (p->k < p->n_local ? p->k : p->n_local);
+  *out = q;
+  return MOE_OK;
+}
+
+#define NEED_PTR(ptr)                                                   \
+  do {                                                                  \
+    if (!(ptr)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #ptr);   \
+  } while (0)
+#define NEED_ALIGNED(ptr)                                                              \
+  do {                                                                                 \
+    if (!aligned16(ptr)) return fail(MOE_ERR_UNSUPPORTED, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+
+// Workspace layout of moe_layer (each region 256-byte aligned).
+struct LayerWs {
+  size_t route, idx, w, counts, offsets, perm, inv, disp, xp, h, yp, total;
+};
+
+LayerWs layer_ws(const moe::Prob& p) {
+  LayerWs L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const size_t es = p.elem();
+  L.route = take(moe::route_ws_bytes(p));
+  L.idx = take(p.tk() * 4);
+  L.w = take(p.tk() * 4);
+  L.counts = take((size_t)p.E * 4);
+  L.offsets = take((size_t)(p.n + 1) * 4);
+  L.perm = take((size_t)p.rows_max * 4);
+  L.inv = take(p.tk() * 4);
+  L.disp = take(moe::dispatch_ws_bytes(p));
+  L.xp = take((size_t)p.rows_max * p.d * es);
+  L.h = take((size_t)p.rows_max * p.f * es);
+  L.yp = take((size_t)p.rows_max * p.d * es);
+  L.total = o + moe::expert_gemm_ws_bytes(p);
+  return L;
+}
+
+size_t call_ws_bytes(const moe::Prob& p, int32_t call) {
+  switch (call) {
+    case MOE_CALL_ROUTE: return moe::route_ws_bytes(p);
+    case MOE_CALL_DISPATCH: return moe::dispatch_ws_bytes(p);
+    case MOE_CALL_EXPERT_GEMM: return moe::expert_gemm_ws_bytes(p);
+    case MOE_CALL_COMBINE: return 0;
+    case MOE_CALL_LAYER: return layer_ws(p).total;
+    default: return 0;
+  }
+}
+
+moe_status_t check_ws(const moe::Prob& p, int32_t call, const void* ws, size_t bytes) {
+  const size_t need = call_ws_bytes(p, call);
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct StreamEvents {
+  hipEvent_t a = nullptr, b = nullptr;
+  int device = -1;
+};
+thread_local StreamEvents g_ev;
+
+hipError_t events_for_current_device(StreamEvents& ev) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (ev.device == dev && ev.a && ev.b) return hipSuccess;
+  if (ev.a) (void)hipEventDestroy(ev.a);
+  if (ev.b) (void)hipEventDestroy(ev.b);
+  ev.a = ev.b = nullptr;
+  e = hipEventCreateWithFlags(&ev.a, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev.b, hipEventDisableTiming);
+  if (e == hipSuccess) ev.device = dev;
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+
+size_t moe_workspace_bytes(const moe_problem_t* p, int32_t call) {
+  moe::Prob q;
+  if (check_problem(p, &q) != MOE_OK) return 0;
+  if (call < MOE_CALL_ROUTE || call > MOE_CALL_LAYER) {
+    fail(MOE_ERR_INVALID_ARG, "unknown call %d", call);
+    return 0;
+  }
+  g_err.clear();
+  return call_ws_bytes(q, call);
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
+                       const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  NEED_PTR(x);
+  NEED_PTR(w_gate);
+  NEED_PTR(topk_idx);
+  NEED_PTR(topk_w);
+  NEED_ALIGNED(x);
+  NEED_ALIGNED(w_gate);
+  if ((st = check_ws(q, MOE_CALL_ROUTE, workspace, workspace_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(moe::launch_route(q, x, w_gate, bias, logits, topk_idx, topk_w, workspace,
+                                      (hipStream_t)stream),
+                    "moe_route");
+}
+
+moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, const void* x,
+                          int32_t* counts_all, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          void* x_packed, void* workspace, size_t workspace_bytes, void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  NEED_PTR(topk_idx);
+  NEED_PTR(x);
+  NEED_PTR(counts_all);
+  NEED_PTR(offsets);
+  NEED_PTR(perm);
+  NEED_PTR(inv);
+  NEED_PTR(x_packed);
+  NEED_ALIGNED(x);
+  NEED_ALIGNED(x_packed);
+  if ((st = check_ws(q, MOE_CALL_DISPATCH, workspace, workspace_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = moe::launch_dispatch_index(q, topk_idx, counts_all, offsets, perm, inv, workspace, s);
+  if (e == hipSuccess) e = moe::launch_gather(q, x, offsets, perm, x_packed, 0, q.n, s);
+  return hip_status(e, "moe_dispatch");
+}
+
+moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* w2, void* h,
+                             void* y_packed, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  NEED_PTR(x_packed);
+  NEED_PTR(offsets);
+  NEED_PTR(w1);
+  NEED_PTR(w3);
+  NEED_PTR(w2);
+  NEED_PTR(h);
+  NEED_PTR(y_packed);
+  NEED_ALIGNED(x_packed);
+  NEED_ALIGNED(w1);
+  NEED_ALIGNED(w3);
+  NEED_ALIGNED(w2);
+  NEED_ALIGNED(h);
+  NEED_ALIGNED(y_packed);
+  if ((st = check_ws(q, MOE_CALL_EXPERT_GEMM, workspace, workspace_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(moe::launch_expert_gemm(q, x_packed, offsets, w1, w3, w2, h, y_packed, workspace,
+                                            0, q.n, (hipStream_t)stream),
+                    "moe_expert_gemm");
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int32_t* inv,
+                         const float* topk_w, void* y, void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  NEED_PTR(y_packed);
+  NEED_PTR(inv);
+  NEED_PTR(topk_w);
+  NEED_PTR(y);
+  NEED_ALIGNED(y_packed);
+  NEED_ALIGNED(y);
+  (void)hipGetLastError();
+  return hip_status(moe::launch_combine(q, y_packed, inv, topk_w, y, (hipStream_t)stream),
+                    "moe_combine");
+}
+
+moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate,
+                       const float* bias, const void* w1, const void* w3, const void* w2,
+                       void* y, const moe_routing_out_t* routing_out, void* workspace,
+                       size_t workspace_bytes, void* stream, void* stream2) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  NEED_PTR(x);
+  NEED_PTR(w_gate);
+  NEED_PTR(w1);
+  NEED_PTR(w3);
+  NEED_PTR(w2);
+  NEED_PTR(y);
+  NEED_ALIGNED(x);
+  NEED_ALIGNED(w_gate);
+  NEED_ALIGNED(w1);
+  NEED_ALIGNED(w3);
+  NEED_ALIGNED(w2);
+  NEED_ALIGNED(y);
+  if ((q.flags & MOE_F_WRITE_LOGITS) && !(routing_out && routing_out->logits))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_WRITE_LOGITS needs routing_out->logits");
+  if ((st = check_ws(q, MOE_CALL_LAYER, workspace, workspace_bytes)) != MOE_OK) return st;
+
+  const LayerWs L = layer_ws(q);
+  char* ws = static_cast<char*>(workspace);
+  auto pick = [&](auto* user, size_t off) {
+    using T = std::remove_pointer_t<decltype(user)>;
+    return user ? user : reinterpret_cast<T*>(ws + off);
+  };
+  const moe_routing_out_t none{};
+  const moe_routing_out_t& ro = routing_out ? *routing_out : none;
+  int32_t* idx = pick(ro.topk_idx, L.idx);
+  float* w = pick(ro.topk_w, L.w);
+  int32_t* counts = pick(ro.counts_all, L.counts);
+  int32_t* offsets = pick(ro.offsets, L.offsets);
+  int32_t* perm = pick(ro.perm, L.perm);
+  int32_t* inv = pick(ro.inv, L.inv);
+  float* logits = (q.flags & MOE_F_WRITE_LOGITS) ? ro.logits : nullptr;
+  void* xp = ws + L.xp;
+  void* h = ws + L.h;
+  void* yp = ws + L.yp;
+  hipStream_t s0 = (hipStream_t)stream;
+  hipStream_t s1 = (hipStream_t)stream2;
+  const bool overlap = (q.flags & MOE_F_OVERLAP) && s1 != nullptr && q.n >= 2;
+
+  (void)hipGetLastError();
+  hipError_t e = moe::launch_route(q, x, w_gate, bias, logits, idx, w, ws + L.route, s0);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch_index(q, idx, counts, offsets, perm, inv, ws + L.disp, s0);
+  if (e != hipSuccess) return hip_status(e, "moe_layer routing");
+  if (!overlap) {
+    e = moe::launch_gather(q, x, offsets, perm, xp, 0, q.n, s0);
+    if (e == hipSuccess)
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.total, 0, q.n, s0);
+  } else {
+    // two-stream dispatch overlap: the upper half of the local experts is
+    // packed on s1 while the lower half's GEMMs run on s0.
+    const int half = q.n / 2;
+    e = events_for_current_device(g_ev);
+    if (e == hipSuccess) e = hipEventRecord(g_ev.a, s0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s1, g_ev.a, 0);
+    if (e == hipSuccess) e = moe::launch_gather(q, x, offsets, perm, xp, half, q.n, s1);
+    if (e == hipSuccess) e = hipEventRecord(g_ev.b, s1);
+    if (e == hipSuccess) e = moe::launch_gather(q, x, offsets, perm, xp, 0, half, s0);
+    if (e == hipSuccess)
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.total, 0, half, s0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s0, g_ev.b, 0);
+    if (e == hipSuccess)
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.total, half, q.n, s0);
+  }
+  if (e == hipSuccess) e = moe::launch_combine(q, yp, inv, w, y, s0);
+  return hip_status(e, "moe_layer");
+}
+
+}  // extern "C"

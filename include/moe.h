@@ -1,0 +1,207 @@
+/*
+ * moe.h -- C ABI of libmoe: one GPU's share of a Mixture-of-Experts layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the DeepSeek-V3 MoE workload of "CUCo: An Agentic Framework for
+ * Compute and Communication Co-design" (Abstract; Table 4, row "MoE
+ * Dispatch/Combine"): tokens are routed to experts, dispatched into
+ * per-expert, variable-size, unpadded buffers, run through the local ("self")
+ * experts, and combined back.  This library computes the share of one GPU that
+ * owns experts [expert_lo, expert_lo + n_local) of E, for all T tokens:
+ *
+ *   moe_route        logits = x W_g (+ b); top-k softmax gating
+ *   moe_dispatch     per-expert histogram, prefix scan, stable permutation,
+ *                    row gather into expert-contiguous buffers
+ *   moe_expert_gemm  SwiGLU expert FFNs as grouped GEMMs over the segments
+ *   moe_combine      weighted un-permute and sum back to token order
+ *   moe_layer        all of the above, stream-ordered
+ *
+ * The pages state no formulas; the definitions below are the plain MoE layer
+ * (softmax top-k gating renormalised over the selected k, ties to the lower
+ * expert index; SwiGLU experts; weighted combine).
+ *
+ * Conventions for every call
+ *   - Tensors are dense, row-major, and live in device memory.  Rows of x,
+ *     x_packed, h, y_packed and y must start on 16-byte boundaries: the base
+ *     pointers must be 16-byte aligned and d, f must be multiples of 8.
+ *   - The caller owns all memory.  The library never allocates device memory
+ *     and never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *     Every call is asynchronous on its stream and never synchronises the
+ *     device or the host.
+ *   - Validation is host-side and shape-only.  On error nothing is launched,
+ *     a status is returned and moe_last_error() describes it.  Data-dependent
+ *     conditions are not checked: NaN/Inf inputs and expert indices outside
+ *     [0, E) in a caller-supplied topk_idx are undefined behaviour.
+ *   - Results are bitwise deterministic for identical inputs and launch
+ *     configuration (no floating-point atomics).
+ *   - The calls are re-entrant; concurrent calls must not share workspace.
+ *   - The number of local assignments A never leaves the device; a caller that
+ *     wants it reads offsets[n_local].
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, k > E, bad expert range */
+  MOE_ERR_UNSUPPORTED = 2, /* d or f not a multiple of 8, k > 32, E > 1024, bad dtype, misaligned */
+  MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4          /* a HIP launch/runtime call failed; message in moe_last_error() */
+};
+
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+
+/* flags */
+enum {
+  MOE_F_WRITE_LOGITS = 1u, /* moe_layer: also write fp32 logits to routing_out->logits */
+  MOE_F_OVERLAP = 2u       /* moe_layer: pack the second half of the local experts on
+                              stream2 while the first half's GEMMs run on stream */
+};
+
+/* Which call a workspace size is asked for. */
+enum {
+  MOE_CALL_ROUTE = 0,
+  MOE_CALL_DISPATCH = 1,
+  MOE_CALL_EXPERT_GEMM = 2,
+  MOE_CALL_COMBINE = 3,
+  MOE_CALL_LAYER = 4
+};
+
+/*
+ * Problem description.
+ *   T          tokens (rows of x)
+ *   d          hidden size
+ *   E          routed experts in total (1..1024)
+ *   k          experts per token (1..min(E, 32))
+ *   f          SwiGLU intermediate size per expert
+ *   expert_lo  first expert owned by this GPU
+ *   n_local    experts owned by this GPU (expert_lo + n_local <= E)
+ *   dtype      MOE_DTYPE_BF16: x, w_gate, w1, w3, w2, x_packed, h, y_packed, y
+ *              are bf16 and all sums accumulate in fp32;
+ *              MOE_DTYPE_F32: all of them are fp32.
+ *   flags      MOE_F_* (read by moe_layer only)
+ * Derived: rows_max = T * min(k, n_local), an upper bound of A.
+ */
+typedef struct moe_problem_t {
+  int32_t T, d, E, k, f, expert_lo, n_local;
+  int32_t dtype;
+  uint32_t flags;
+} moe_problem_t;
+
+/* Optional device outputs of moe_layer; any member may be NULL. */
+typedef struct moe_routing_out_t {
+  int32_t* topk_idx;   /* [T,k] */
+  float* topk_w;       /* [T,k] */
+  float* logits;       /* [T,E], written only with MOE_F_WRITE_LOGITS */
+  int32_t* counts_all; /* [E] */
+  int32_t* offsets;    /* [n_local+1] */
+  int32_t* perm;       /* [rows_max], first A entries valid */
+  int32_t* inv;        /* [T*k] */
+} moe_routing_out_t;
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+/*
+ * Bytes of device scratch that `call` (MOE_CALL_*) needs for problem p, or 0
+ * when p is invalid (then moe_last_error() says why) or the call needs none.
+ * The workspace pointer passed to a call must be 256-byte aligned.
+ */
+size_t moe_workspace_bytes(const moe_problem_t* p, int32_t call);
+
+/*
+ * Router: logits[t,e] = sum_i x[t,i] * w_gate[i,e] (+ bias[e]) accumulated in
+ * fp32; then per token the k largest logits in descending order, ties to the
+ * lower expert index, and weights w_j = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ * (softmax over all E renormalised over the selected k).  The pages call this
+ * step the routing of the DeepSeek-V3 MoE layer (gist.science summary of the
+ * CUCo paper, §4 Results: "imbalanced sparse routing").
+ *   x        [T,d]   dtype
+ *   w_gate   [d,E]   dtype
+ *   bias     [E]     fp32, or NULL
+ *   logits   [T,E]   fp32 output, or NULL
+ *   topk_idx [T,k]   int32 output
+ *   topk_w   [T,k]   fp32 output
+ *   workspace of moe_workspace_bytes(p, MOE_CALL_ROUTE) bytes (may be NULL if 0)
+ */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate,
+                       const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dispatch (CUCo, Table 4, "MoE Dispatch/Combine": variable-size per-peer
+ * transfers with no padding).  Assignment a = t*k + j is local when
+ * expert_lo <= topk_idx[a] < expert_lo + n_local.
+ *   counts_all [E]          counts_all[e] = #assignments to expert e (all E)
+ *   offsets    [n_local+1]  offsets[0] = 0, offsets[e+1] = offsets[e] + counts_all[expert_lo+e]
+ *   perm       [rows_max]   perm[p] = a, local assignments sorted by local expert,
+ *                           ties in ascending a (stable); entries >= A untouched
+ *   inv        [T*k]        inv[perm[p]] = p; -1 for non-local assignments
+ *   x_packed   [rows_max,d] x_packed[p] = x[perm[p] / k]; rows >= A untouched
+ *   workspace of moe_workspace_bytes(p, MOE_CALL_DISPATCH) bytes
+ */
+moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, const void* x,
+                          int32_t* counts_all, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          void* x_packed, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Local expert compute (CUCo, Abstract: "local compute" of the MoE layer).
+ * For each local expert e and its rows R = [offsets[e], offsets[e+1]):
+ *   h[R]        = rnd(SiLU(x_packed[R] w1[e]) * (x_packed[R] w3[e]))
+ *   y_packed[R] = rnd(h[R] w2[e])
+ * with SiLU(z) = z / (1 + exp(-z)), fp32 accumulation, and rnd = round to
+ * nearest even into the problem dtype.
+ *   w1, w3  [n_local,d,f]  dtype
+ *   w2      [n_local,f,d]  dtype
+ *   h       [rows_max,f]   dtype output (rows >= A untouched)
+ *   y_packed[rows_max,d]   dtype output (rows >= A untouched)
+ *   workspace of moe_workspace_bytes(p, MOE_CALL_EXPERT_GEMM) bytes
+ */
+moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* w2, void* h,
+                             void* y_packed, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Combine (CUCo, Table 4, "MoE Dispatch/Combine"): un-permute and weighted sum,
+ *   y[t] = rnd(sum over j < k with inv[t*k+j] >= 0 of topk_w[t,j] * y_packed[inv[t*k+j]])
+ * accumulated in fp32 in slot order.  A token with no local slot gets an exact
+ * zero row; every row of y is written.
+ *   y_packed [rows_max,d] dtype;  inv [T*k];  topk_w [T,k] fp32;  y [T,d] dtype
+ */
+moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int32_t* inv,
+                         const float* topk_w, void* y, void* stream);
+
+/*
+ * The whole layer: moe_route, moe_dispatch, moe_expert_gemm, moe_combine in
+ * stream order on `stream`, with all intermediates in `workspace`
+ * (moe_workspace_bytes(p, MOE_CALL_LAYER) bytes).  No device-to-host
+ * synchronisation.  routing_out may be NULL; its non-NULL members receive
+ * copies of the routing and dispatch tensors.  With MOE_F_OVERLAP and a
+ * non-NULL stream2, the row gather of the upper half of the local experts runs
+ * on stream2 while the lower half's GEMMs run on `stream` (the two-stream
+ * dispatch overlap of CUCo, Abstract and Table 4); stream2 is joined back into
+ * `stream` before the call returns its work.
+ */
+moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate,
+                       const float* bias, const void* w1, const void* w3, const void* w2,
+                       void* y, const moe_routing_out_t* routing_out, void* workspace,
+                       size_t workspace_bytes, void* stream, void* stream2);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

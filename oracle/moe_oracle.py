@@ -268,21 +268,28 @@ def token_outputs(p, inputs: Dict[str, np.ndarray], topk_idx: np.ndarray, topk_w
     rows of ``moe_layer`` and lets a full-size run be checked on a sample.
     """
     dt = p.dtype
-    X = widen(np.asarray(inputs["x"])[list(tokens)], dt)
+    tokens = list(tokens)
+    X = widen(np.asarray(inputs["x"])[tokens], dt)
     idx = np.asarray(topk_idx)
     W = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    # expert output of every (sampled token, local slot), one expert at a time
+    # so that only one expert's float64 weights are held at once
+    yslot = {}
+    for e in range(p.n_local):
+        pairs = [(r, j) for r, t in enumerate(tokens) for j in range(p.k)
+                 if int(idx[t, j]) - p.expert_lo == e]
+        if not pairs:
+            continue
+        rows = np.array([r for r, _ in pairs])
+        _, y = _expert_rows(X[rows], widen(inputs["w1"][e], dt), widen(inputs["w3"][e], dt),
+                            widen(inputs["w2"][e], dt), dt)
+        for q, rj in enumerate(pairs):
+            yslot[rj] = y[q]
     out = np.zeros((len(tokens), p.d), dtype=np.float64)
-    cache = {}
     for r, t in enumerate(tokens):
         acc = np.zeros(p.d, dtype=np.float64)
-        for j in range(p.k):
-            e = int(idx[t, j]) - p.expert_lo
-            if not 0 <= e < p.n_local:
-                continue
-            if e not in cache:
-                cache[e] = (widen(inputs["w1"][e], dt), widen(inputs["w3"][e], dt),
-                            widen(inputs["w2"][e], dt))
-            _, y = _expert_rows(X[r:r + 1], *cache[e], dt)
-            acc += W[t, j] * y[0]
+        for j in range(p.k):                     # slot order
+            if (r, j) in yslot:
+                acc += W[t, j] * yslot[(r, j)]
         out[r] = rnd(acc, dt)
     return out

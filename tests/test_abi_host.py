@@ -1,0 +1,155 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+The library must load, export every function declared in include/moe.h, and
+reject invalid calls with the documented status before touching HIP.  Fake
+device addresses are fine here: validation fails before anything is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import combine_router_top_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH), reason="libmoe.so not built")
+
+FAKE = 0x10000  # 16-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    L = ctypes.CDLL(M.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == set(M.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert M.lib().moe_version().startswith(b"libmoe")
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _p(**kw):
+    base = dict(T=64, d=128, E=8, k=2, f=256, expert_lo=0, n_local=8, dtype=M.MOE_DTYPE_F32, flags=0)
+    base.update(kw)
+    return M.Problem(**base)
+
+
+def _route(p, x=FAKE, wg=FAKE, idx=FAKE, w=FAKE, ws=FAKE, wsb=1 << 30):
+    return M.lib().moe_route(ctypes.byref(p), x, wg, None, None, idx, w, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), M.MOE_ERR_INVALID_ARG),
+    (dict(d=-8), M.MOE_ERR_INVALID_ARG),
+    (dict(k=9), M.MOE_ERR_INVALID_ARG),            # k > E
+    (dict(k=0), M.MOE_ERR_INVALID_ARG),
+    (dict(expert_lo=4, n_local=5), M.MOE_ERR_INVALID_ARG),
+    (dict(n_local=0), M.MOE_ERR_INVALID_ARG),
+    (dict(expert_lo=-1), M.MOE_ERR_INVALID_ARG),
+    (dict(flags=0x80), M.MOE_ERR_INVALID_ARG),
+    (dict(d=100), M.MOE_ERR_UNSUPPORTED),          # d % 8
+    (dict(f=12), M.MOE_ERR_UNSUPPORTED),           # f % 8
+    (dict(E=64, k=33, n_local=64), M.MOE_ERR_UNSUPPORTED),
+    (dict(E=1025, n_local=8), M.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), M.MOE_ERR_UNSUPPORTED),
+])
+def test_problem_validation(kw, status):
+    assert _route(_p(**kw)) == status
+    assert M.lib().moe_last_error()
+    assert M.lib().moe_workspace_bytes(ctypes.byref(_p(**kw)), M.MOE_CALL_LAYER) == 0
+
+
+def test_null_problem():
+    assert M.lib().moe_route(None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        M.MOE_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers():
+    p = _p()
+    assert _route(p, x=0) == M.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in M.lib().moe_last_error()
+    assert _route(p, idx=0) == M.MOE_ERR_INVALID_ARG
+    assert _route(p, x=FAKE + 2) == M.MOE_ERR_UNSUPPORTED
+    assert b"aligned" in M.lib().moe_last_error()
+    L = M.lib()
+    assert L.moe_combine(ctypes.byref(p), FAKE, 0, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_gemm(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 0,
+                             None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30,
+                          None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_checks():
+    p = _p()
+    need = M.lib().moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_ROUTE)
+    assert need >= 64 * 8 * 4
+    assert _route(p, ws=0) == M.MOE_ERR_WORKSPACE
+    assert _route(p, wsb=need - 1) == M.MOE_ERR_WORKSPACE
+    assert _route(p, ws=FAKE + 16) == M.MOE_ERR_WORKSPACE       # not 256-byte aligned
+    L = M.lib()
+    lay = L.moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_LAYER)
+    assert lay > need
+    assert L.moe_layer(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                       lay - 1, None, None) == M.MOE_ERR_WORKSPACE
+    assert L.moe_workspace_bytes(ctypes.byref(p), 99) == 0
+
+
+def test_write_logits_needs_buffer():
+    p = _p(flags=M.MOE_F_WRITE_LOGITS)
+    L = M.lib()
+    lay = L.moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_LAYER)
+    assert L.moe_layer(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, lay,
+                       None, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_cover_worst_case():
+    """The layer workspace holds every intermediate at rows_max = T*min(k, n_local)."""
+    for (T, d, E, k, f, lo, n, dt) in [(4096, 7168, 256, 8, 2048, 0, 32, 1),
+                                       (16384, 4096, 8, 2, 14336, 0, 8, 1),
+                                       (64, 128, 8, 2, 256, 0, 8, 0)]:
+        p = M.Problem(T, d, E, k, f, lo, n, dt, 0)
+        es = 2 if dt == 1 else 4
+        rows = T * min(k, n)
+        lay = M.lib().moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_LAYER)
+        assert lay >= rows * (2 * d + f) * es + rows * 4 + 3 * T * k * 4
+
+
+def test_hip_error_path_without_gpu():
+    """A valid call on a machine with no GPU returns MOE_ERR_HIP with a message
+    (run in a child process so the HIP runtime state stays out of this one)."""
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import combine_router_top_amd as M
+p = M.Problem(64, 128, 8, 2, 256, 0, 8, 0, 0)
+L = M.lib()
+n = L.moe_workspace_bytes(ctypes.byref(p), 0)
+st = L.moe_route(ctypes.byref(p), 0x10000, 0x10000, None, None, 0x10000, 0x10000, 0x10000, n, None)
+print(st, L.moe_last_error().decode())
+""" % ROOT
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is visible")
+    except ImportError:
+        pass
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
+    assert r.returncode == 0, r.stderr
+    st, msg = r.stdout.split(" ", 1)
+    assert int(st) == M.MOE_ERR_HIP and "moe_route" in msg

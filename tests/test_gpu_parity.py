@@ -1,0 +1,211 @@
+"""GPU parity: every call of libmoe against the CPU oracle, on seeded inputs
+small enough for the full oracle but spanning several tiles and ragged tails.
+
+Bars: routing indices, counts, offsets, permutation and gathered rows
+bit-exact; logits and gate weights within 1e-5; expert and layer outputs within
+the floored relative error 2e-2 (bf16) or 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+
+import combine_router_top_amd as M
+import oracle.moe_oracle as O
+import workloads
+from tests.gpu_util import check_close, check_routing, dev, host
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+SMALL = {
+    # name: workload (shapes chosen to hit every kernel variant and tail)
+    "tiny_fp32": workloads.get("tiny_fp32"),
+    "wide_tails": W("wide_tails", 300, 264, 64, 6, 200, 8, 20, "bf16", seed=3),
+    "wide_dsv3_like": W("wide_dsv3_like", 200, 512, 256, 8, 256, 0, 32, "bf16", seed=4),
+    "narrow_multiblock": W("narrow_multiblock", 777, 256, 8, 2, 320, 0, 8, "bf16", seed=5),
+    "skew": W("skew", 512, 128, 32, 4, 128, 0, 16, "bf16", skew=True, seed=6),
+    "plain_router_bf16": W("plain_router_bf16", 100, 64, 22, 3, 64, 5, 10, "bf16", seed=7),
+    "fp32_mid": W("fp32_mid", 130, 72, 12, 3, 40, 2, 7, "f32", seed=8),
+    "one_token": W("one_token", 1, 64, 16, 1, 32, 0, 16, "bf16", seed=9),
+    "one_local": W("one_local", 257, 128, 16, 4, 64, 15, 1, "bf16", seed=10),
+    "dense_e1": W("dense_e1", 70, 96, 1, 1, 136, 0, 1, "bf16", seed=11),
+    "k_equals_e": W("k_equals_e", 90, 64, 6, 6, 48, 1, 4, "bf16", seed=12),
+}
+
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        w = SMALL[name]
+        inp = workloads.generate(w)
+        ref = O.moe_layer(w, inp)
+        d = {k: dev(v) for k, v in inp.items()}
+        _cache[name] = (w, inp, ref, d)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_route(name):
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, wt, logits = M.route(p, d["x"], d["w_gate"], d["bias"], want_logits=True)
+    check_routing(w, host(logits), host(idx), host(wt), ref["logits"])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16"])
+def test_route_integer_inputs_exact(name):
+    """Small-integer x and W_g: logits are exact on both sides, so routing,
+    including ties, must match with no exemption."""
+    w = SMALL[name]
+    ii = workloads.integer_inputs(w)
+    p = M.Spec.of(w)
+    idx, wt, logits = M.route(p, dev(ii["x"]), dev(ii["w_gate"]), None, want_logits=True)
+    ref_l = O.router_logits(ii["x"], ii["w_gate"], w.dtype)
+    assert np.array_equal(host(logits), ref_l)
+    check_routing(w, host(logits), host(idx), host(wt), ref_l, tau=0)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_dispatch(name):
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, _ = M.route(p, d["x"], d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, d["x"])
+    counts, offsets, perm, inv = O.local_dispatch(host(idx), w.E, w.expert_lo, w.n_local)
+    A = int(offsets[-1])
+    assert np.array_equal(host(o["counts_all"]), counts)
+    assert np.array_equal(host(o["offsets"]), offsets)
+    gp = host(o["perm"])
+    assert np.array_equal(gp[:A], perm)
+    assert np.all(gp[A:] == -7), "rows past A must be untouched"
+    assert np.array_equal(host(o["inv"]), inv)
+    xp = host(o["x_packed"])
+    assert np.array_equal(xp[:A], O.gather_rows(inp["x"], perm, w.k))
+    assert not np.any(xp[A:]), "rows past A must be untouched"
+
+
+@pytest.mark.parametrize("pattern", ["random", "all_one_expert", "none_local", "sorted", "reversed"])
+def test_dispatch_supplied_indices(pattern):
+    """Dispatch on caller-supplied routing with extreme distributions."""
+    T, d, E, k, lo, n = 3000, 64, 40, 5, 7, 13
+    rng = np.random.default_rng(21)
+    if pattern == "random":
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)])
+    elif pattern == "all_one_expert":
+        idx = np.tile(np.array([lo + 3, 0, 1, 2, 3]), (T, 1))
+    elif pattern == "none_local":
+        idx = np.tile(np.array([0, 1, 2, 3, 4]), (T, 1))
+    elif pattern == "sorted":
+        idx = np.tile(np.arange(lo, lo + k), (T, 1))
+    else:
+        idx = np.tile(np.arange(lo + n - 1, lo + n - 1 - k, -1), (T, 1))
+    idx = idx.astype(np.int32)
+    x = rng.integers(0, 65535, size=(T, d), dtype=np.uint16) & np.uint16(0x7F7F)
+    p = M.Spec(T, d, E, k, 64, lo, n, "bf16")
+    o = M.dispatch(p, dev(idx), dev(x))
+    counts, offsets, perm, inv = O.local_dispatch(idx, E, lo, n)
+    A = int(offsets[-1])
+    assert np.array_equal(host(o["counts_all"]), counts)
+    assert np.array_equal(host(o["offsets"]), offsets)
+    assert np.array_equal(host(o["perm"])[:A], perm)
+    assert np.array_equal(host(o["inv"]), inv)
+    assert np.array_equal(host(o["x_packed"])[:A], x[perm // k])
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_combine_identity_experts(name):
+    """y_packed := x_packed gives y = rnd(x * sum of local weights); with all
+    experts local the bf16 output equals x bit for bit."""
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, d["x"])
+    y = host(M.combine(p, o["x_packed"], o["inv"], wt))
+    yr = O.combine(O.widen(host(o["x_packed"]), w.dtype), host(o["inv"]), host(wt), w.dtype)
+    check_close(O.widen(y, w.dtype), yr, w.dtype, "combine")
+    inv = host(o["inv"]).reshape(w.T, w.k)
+    none = ~(inv >= 0).any(1)
+    assert np.all(O.widen(y, w.dtype)[none] == 0)
+    if w.n_local == w.E and w.dtype == "bf16":
+        assert np.array_equal(y, inp["x"])
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_expert_gemm(name):
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, d["x"])
+    h, yp = M.expert_gemm(p, o["x_packed"], o["offsets"], d["w1"], d["w3"], d["w2"])
+    offsets = host(o["offsets"])
+    A = int(offsets[-1])
+    hr, ypr = O.swiglu_experts(host(o["x_packed"])[:A], offsets, inp["w1"], inp["w3"], inp["w2"], w.dtype)
+    check_close(O.widen(host(h)[:A], w.dtype), hr, w.dtype, "h")
+    check_close(O.widen(host(yp)[:A], w.dtype), ypr, w.dtype, "y_packed")
+    assert not np.any(host(h)[A:]) and not np.any(host(yp)[A:]), "rows past A must be untouched"
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+@pytest.mark.parametrize("overlap", [False, True])
+def test_layer(name, overlap):
+    import torch
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    s2 = torch.cuda.Stream() if overlap else None
+    y, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True,
+                   want_logits=True, overlap=overlap, stream2=s2)
+    torch.cuda.synchronize()
+    check_routing(w, host(r["logits"]), host(r["topk_idx"]), host(r["topk_w"]), ref["logits"])
+    routing = {"topk_idx": host(r["topk_idx"]), "topk_w": host(r["topk_w"])}
+    oref = O.moe_layer(w, inp, routing=routing)
+    assert np.array_equal(host(r["counts_all"]), oref["counts_all"])
+    assert np.array_equal(host(r["offsets"]), oref["offsets"])
+    A = int(oref["offsets"][-1])
+    assert np.array_equal(host(r["perm"])[:A], oref["perm"])
+    assert np.array_equal(host(r["inv"]), oref["inv"])
+    check_close(O.widen(host(y), w.dtype), oref["y"], w.dtype, "y")
+
+
+def test_layer_deterministic_and_overlap_identical():
+    import torch
+    w, inp, ref, d = case("wide_dsv3_like")
+    p = M.Spec.of(w)
+    outs = []
+    for ov in (False, False, True):
+        s2 = torch.cuda.Stream() if ov else None
+        y, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True,
+                       want_logits=True, overlap=ov, stream2=s2)
+        torch.cuda.synchronize()
+        outs.append({"y": host(y), **{k: host(v) for k, v in r.items()}})
+    for o in outs[1:]:
+        for k in outs[0]:
+            assert np.array_equal(outs[0][k], o[k]), k
+
+
+@pytest.mark.parametrize("name", ["wide_dsv3_like", "narrow_multiblock", "fp32_mid"])
+def test_layer_token_shuffle_equivariance(name):
+    """Permuting tokens permutes routing and outputs; bit-exact because each
+    row's reductions do not depend on the other rows."""
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    y, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True)
+    sh = np.random.default_rng(5).permutation(w.T)
+    x2 = dev(inp["x"][sh])
+    y2, r2 = M.layer(p, x2, d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True)
+    assert np.array_equal(host(r2["topk_idx"]), host(r["topk_idx"])[sh])
+    assert np.array_equal(host(r2["topk_w"]), host(r["topk_w"])[sh])
+    assert np.array_equal(host(y2), host(y)[sh])
+
+
+def test_layer_no_local_tokens():
+    """A bias that keeps every token off the local experts: A = 0 and y = 0."""
+    w = W("no_local", 64, 64, 16, 2, 32, 8, 8, "bf16", seed=13)
+    inp = workloads.generate(w)
+    bias = np.zeros(16, dtype=np.float32)
+    bias[8:] = -1e4
+    p = M.Spec.of(w)
+    y, r = M.layer(p, dev(inp["x"]), dev(inp["w_gate"]), dev(bias), dev(inp["w1"]), dev(inp["w3"]),
+                   dev(inp["w2"]), routing=True)
+    assert int(host(r["offsets"])[-1]) == 0
+    assert np.all(host(r["inv"]) == -1)
+    assert not np.any(host(y))
