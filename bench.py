@@ -1,0 +1,262 @@
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one moe_layer call (router, dispatch, SwiGLU grouped GEMMs,
+combine) over the workload's T tokens, inputs already resident in HBM.
+Prints one JSON line:
+
+  value         tokens/s of the whole layer (T / mean step time)
+  roofline      the dominant kernel (the grouped GEMM, moe_expert_gemm: the
+                SwiGLU GEMM-1 launch plus the down-projection GEMM-2 launch)
+                against MI355X's published peak: algorithmic bytes (or flops)
+                per call / mean call time measured with HIP events on its
+                stream; traffic = HBM bytes from rocprofv3 FETCH_SIZE and
+                WRITE_SIZE when a counter summary for the current kernel source
+                is committed under profiles/, else null
+  phases        every ABI call timed the same way, with its own roofline
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+
+This build runs on one GPU only; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense flop/s
+METRIC = "MoE layer tokens/s on 1 MI355X; grouped-GEMM % MFMA peak, dispatch % HBM"
+GEMM_SOURCES = ["expert_gemm.hip", "mfma_tile.h", "common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--overlap", action="store_true", help="two-stream dispatch overlap")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    return ap.parse_args()
+
+
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for n in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "combine_router_top_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per moe_expert_gemm call from a committed counter summary,
+    only if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_expert_gemm_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != gemm_source_hash():
+        return None
+    return t.get("hbm_bytes_per_call")
+
+
+def work_model(w, A, active, s):
+    """Algorithmic bytes and flops per call (what the method must move or
+    compute; not the dense work it skips)."""
+    T, d, E, k, f = w.T, w.d, w.E, w.k, w.f
+    return {
+        "route": {"bytes": T * d * s + d * E * s + 8 * T * k, "flops": 2 * T * d * E},
+        "dispatch": {"bytes": 4 * T * k + 4 * (A + T * k) + 2 * A * d * s + 4 * E, "flops": 0},
+        "expert_gemm": {"bytes": active * 3 * d * f * s + A * d * s + 2 * A * f * s + A * d * s,
+                        "flops": 6 * A * d * f},
+        "combine": {"bytes": A * d * s + 8 * T * k + T * d * s, "flops": 0},
+    }
+
+
+def roofline(bytes_, flops, sec, dtype):
+    ai = flops / bytes_ if bytes_ else 0.0
+    ridge = MFMA_PEAK[dtype] / HBM_PEAK
+    if flops and ai >= ridge:
+        ach = flops / sec / 1e12
+        peak = MFMA_PEAK[dtype] / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+    ach = bytes_ / sec / 1e9
+    peak = HBM_PEAK / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": peak, "unit": "GB/s", "frac": ach / peak}
+
+
+def cpu_baseline(w, inp, budget):
+    """The oracle, as it stands, on the first Ts tokens of the same workload;
+    Ts doubles while a run stays under budget/4 seconds."""
+    import oracle.moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    Ts = min(w.T, 256)
+    best = None
+    while True:
+        ws = w.replace(T=Ts)
+        sub = dict(inp, x=inp["x"][:Ts])
+        t0 = time.perf_counter()
+        O.moe_layer(ws, sub)
+        dt = time.perf_counter() - t0
+        best = (Ts, dt)
+        if Ts >= w.T or dt > budget / 4:
+            break
+        Ts = min(w.T, Ts * 2)
+    Ts, dt = best
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"full oracle layer (routing, dispatch, SwiGLU experts, combine) on the first "
+                      f"{Ts} of {w.T} tokens of workload {w.name}, float64 numpy, {dt:.2f} s",
+            "seconds": dt, "tokens": Ts}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE {world}); the layer's expert-parallel sharding is a design note, "
+              f"not built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_router_top_amd as M
+    import workloads
+
+    w = workloads.get(a.workload)
+    t0 = time.perf_counter()
+    inp = workloads.generate(w)
+    gen_s = time.perf_counter() - t0
+
+    def dev(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    torch.cuda.set_device(0)
+    d = {k: dev(v) for k, v in inp.items()}
+    p = M.Spec.of(w, M.MOE_F_OVERLAP if a.overlap else 0)
+    stream = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream() if a.overlap else None
+    ws = M.alloc_workspace(p)
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                    device="cuda")
+
+    def step():
+        M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], overlap=a.overlap,
+                workspace=ws, stream=stream, stream2=s2, out=y)
+
+    # routing statistics (outside any timed region)
+    _, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True)
+    torch.cuda.synchronize()
+    offsets = r["offsets"].cpu().numpy()
+    counts = np.diff(offsets)
+    A = int(offsets[-1])
+    active = int((counts > 0).sum())
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # each ABI call on its own, HIP events on the launch stream between calls
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    ws_r = M.alloc_workspace(p, M.MOE_CALL_ROUTE)
+    ws_d = M.alloc_workspace(p, M.MOE_CALL_DISPATCH)
+    M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt))
+    dsp = M.dispatch(p, idx, d["x"], workspace=ws_d)
+    h = torch.empty((w.rows_max, w.f), dtype=y.dtype, device="cuda")
+    yp = torch.empty((w.rows_max, w.d), dtype=y.dtype, device="cuda")
+    names = ["route", "dispatch", "expert_gemm", "combine"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    tot = {n: 0.0 for n in names}
+    iters = max(5, a.steps)
+    for it in range(iters + 2):
+        ev[0].record(stream)
+        M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt))
+        ev[1].record(stream)
+        M.dispatch(p, idx, d["x"], workspace=ws_d, out=dsp)
+        ev[2].record(stream)
+        M.expert_gemm(p, dsp["x_packed"], dsp["offsets"], d["w1"], d["w3"], d["w2"], out=(h, yp))
+        ev[3].record(stream)
+        M.combine(p, yp, dsp["inv"], wt, out=y)
+        ev[4].record(stream)
+        torch.cuda.synchronize()
+        if it >= 2:
+            for j, n in enumerate(names):
+                tot[n] += ev[j].elapsed_time(ev[j + 1])
+    s = 2 if w.dtype == "bf16" else 4
+    model = work_model(w, A, active, s)
+    phases = {}
+    for n in names:
+        sec = tot[n] / iters / 1e3
+        ph = {"ms": sec * 1e3, "bytes": model[n]["bytes"], "flops": model[n]["flops"]}
+        ph.update(roofline(model[n]["bytes"], model[n]["flops"], sec, w.dtype))
+        if model[n]["flops"]:
+            ph["tflops"] = model[n]["flops"] / sec / 1e12
+            ph["mfma_frac"] = model[n]["flops"] / sec / MFMA_PEAK[w.dtype]
+        phases[n] = ph
+
+    g = phases["expert_gemm"]
+    roof = {k: g[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof["kernel"] = "moe_expert_gemm (grouped_gemm_bf16<SwiGLU> + grouped_gemm_bf16<down>)"
+    roof["traffic"] = committed_traffic(w.name)
+    roof["algorithmic_bytes"] = model["expert_gemm"]["bytes"]
+    roof["algorithmic_flops"] = model["expert_gemm"]["flops"]
+
+    out = {
+        "metric": METRIC,
+        "value": w.T / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights; no trained weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
+                   "local_experts": [w.expert_lo, w.expert_lo + w.n_local - 1],
+                   "skew_bias": w.skew, "A_local": A, "active_local_experts": active,
+                   "overlap": a.overlap},
+        "roofline": roof,
+        "phases": phases,
+        "wall_ms_per_step": wall / a.steps * 1e3,
+        "input_gen_s": gen_s,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -180,19 +180,27 @@ def route(p: Spec, x, w_gate, bias=None, want_logits: bool = False, workspace=No
     return (idx, w, logits) if want_logits else (idx, w)
 
 
-def dispatch(p: Spec, topk_idx, x, workspace=None, stream=None) -> Dict[str, object]:
+def dispatch(p: Spec, topk_idx, x, workspace=None, stream=None, out=None) -> Dict[str, object]:
+    """Returns counts_all, offsets, perm, inv, x_packed.  Fresh outputs are
+    pre-filled (perm with -7, x_packed with 0) so that untouched rows are
+    visible; ``out`` (a dict of the same tensors) is written in place."""
     torch = _torch()
     dt = _dt(p)
     _need(topk_idx, (p.T, p.k), torch.int32, "topk_idx")
     _need(x, (p.T, p.d), dt, "x")
     dev = x.device
-    o = {
+    o = out if out is not None else {
         "counts_all": torch.empty(p.E, dtype=torch.int32, device=dev),
         "offsets": torch.empty(p.n_local + 1, dtype=torch.int32, device=dev),
         "perm": torch.full((p.rows_max,), -7, dtype=torch.int32, device=dev),
         "inv": torch.empty(p.T * p.k, dtype=torch.int32, device=dev),
         "x_packed": torch.zeros((p.rows_max, p.d), dtype=dt, device=dev),
     }
+    _need(o["counts_all"], (p.E,), torch.int32, "counts_all")
+    _need(o["offsets"], (p.n_local + 1,), torch.int32, "offsets")
+    _need(o["perm"], (p.rows_max,), torch.int32, "perm")
+    _need(o["inv"], (p.T * p.k,), torch.int32, "inv")
+    _need(o["x_packed"], (p.rows_max, p.d), dt, "x_packed")
     ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_DISPATCH, dev)
     pc = p.c()
     _check(lib().moe_dispatch(ctypes.byref(pc), _ptr(topk_idx), _ptr(x), _ptr(o["counts_all"]),
