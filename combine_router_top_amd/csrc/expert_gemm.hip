@@ -32,34 +32,31 @@ namespace moe {
 
 constexpr int XG_MTMAX = 10;              // m-tiles per row block
 constexpr int XG_BM = 16 * XG_MTMAX;      // rows per row block
-constexpr int XG_KS = 64;                 // K per LDS stage
-constexpr int XG_LDA = XG_KS + 8;         // LDS row stride (bf16), 16-byte pad
+constexpr int XG_KS = 64;                 // K per pipeline stage
+constexpr int XG_LDA = XG_KS + 8;         // LDS row stride (bf16): 144 B, conflict-free fragment reads
+constexpr int XG_NBUF = 3;                // register ring: stage being computed + 2 in flight
 constexpr int XG_MAXN = 1024;             // max local experts
 
-// Row block of this workgroup: expert e, rows [r0, r0 + R).
+// Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb.
 struct RowBlock {
-  int e, r0, R;
+  int e, r0, R, nb;
 };
 
-// Wave 0 scans the per-expert block counts (ceil(count / XG_BM)) over
-// [e_begin, e_end) and locates row block `mb`.  R = 0 when mb is past the end.
-__device__ RowBlock find_row_block(const int32_t* __restrict__ offsets, int e_begin, int e_end,
-                                   int mb, int* sh) {
+// Schedule from `offsets` (computed by every workgroup, a few hundred cycles):
+// expert e in [e_begin, e_end) has ceil(count_e / XG_BM) row blocks, each with
+// nblk_n column blocks.  The G = (total row blocks) * nblk_n live workgroups
+// are renumbered so that every XCD (workgroup id mod 8 on this part) receives
+// a contiguous range of (row block, column block) pairs: all column blocks of
+// one row block then share one L2 for their A rows.  R = 0 means "exit".
+__device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, int e_end,
+                             int nblk_n, int* pre) {
+  const int ne = e_end - e_begin;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int carry = 0;
-    if (lane == 0) {
-      sh[0] = -1;
-      sh[1] = 0;
-      sh[2] = 0;
-    }
-    for (int e0 = e_begin; e0 < e_end; e0 += 64) {
-      const int e = e0 + lane;
-      int cnt = 0, o = 0;
-      if (e < e_end) {
-        o = offsets[e];
-        cnt = offsets[e + 1] - o;
-      }
+    for (int j0 = 0; j0 < ne; j0 += 64) {
+      const int j = j0 + lane;
+      const int cnt = j < ne ? offsets[e_begin + j + 1] - offsets[e_begin + j] : 0;
       const int nb = (cnt + XG_BM - 1) / XG_BM;
       int x = nb;
 #pragma unroll
@@ -67,30 +64,126 @@ __device__ RowBlock find_row_block(const int32_t* __restrict__ offsets, int e_be
         const int y = __shfl_up(x, off);
         if (lane >= off) x += y;
       }
-      const int excl = carry + x - nb;
-      if (e < e_end && mb >= excl && mb < excl + nb) {
-        const int j = mb - excl;
-        sh[0] = e;
-        sh[1] = o + j * XG_BM;
-        sh[2] = min(XG_BM, cnt - j * XG_BM);
-      }
+      if (j < ne) pre[j] = carry + x;
       carry += __shfl(x, 63);
     }
+    if (lane == 0) pre[XG_MAXN] = carry;
   }
   __syncthreads();
-  RowBlock rb{sh[0], sh[1], sh[2]};
+  RowBlock rb{0, 0, 0, 0};
+  const int G = pre[XG_MAXN] * nblk_n;
+  const int b = blockIdx.x;
+  if (b >= G) return rb;
+  const int xcd = b & 7, q = b >> 3;
+  const int L = xcd * (G >> 3) + min(xcd, G & 7) + q;
+  const int mb = L / nblk_n;
+  rb.nb = L - mb * nblk_n;
+  int lo = 0, hi = ne - 1;  // first j with pre[j] > mb
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] > mb) hi = mid; else lo = mid + 1;
+  }
+  const int e = e_begin + lo;
+  const int jb = mb - (lo ? pre[lo - 1] : 0);
+  const int o = offsets[e];
+  const int cnt = offsets[e + 1] - o;
+  rb.e = e;
+  rb.r0 = o + jb * XG_BM;
+  rb.R = min(XG_BM, cnt - jb * XG_BM);
   return rb;
 }
 
-template <bool SWIGLU, int MT>
+// One pipeline stage = 64 of K.  Per stage each lane loads its two 8x4 weight
+// blocks (B) and its share of the A tile (A rows x 64 k) into register ring
+// slot J; the A share is later written to the LDS double buffer.
+template <int MT, bool CHECK>
+struct Pipe {
+  static constexpr int AVEC = 16 * MT * (XG_KS / 8);  // 16-byte A vectors per stage
+  static constexpr int AV = (AVEC + 255) / 256;       // per thread
+  BRaw b[XG_NBUF][2];
+  u32x4 ar[XG_NBUF][AV];
+};
+
+template <int J, int MT, bool CHECK>
+__device__ __forceinline__ void pipe_issue(Pipe<MT, CHECK>& P, int st, int nst,
+                                           const bf16_t* __restrict__ Ablk, int R,
+                                           const bf16_t* __restrict__ Bl, int K, int N, int col) {
+  if (st >= nst) return;
+  const int k0 = st * XG_KS;
+  if (CHECK) {
+    load_b_block(P.b[J][0], Bl, N, k0, K, col, N);
+    load_b_block(P.b[J][1], Bl, N, k0 + 32, K, col, N);
+  } else {
+    load_b_block_nocheck(P.b[J][0], Bl, N, k0, col);
+    load_b_block_nocheck(P.b[J][1], Bl, N, k0 + 32, col);
+  }
+#pragma unroll
+  for (int q = 0; q < Pipe<MT, CHECK>::AV; ++q) {
+    const int v = threadIdx.x + 256 * q;
+    const int r = v >> 3, s = v & 7;
+    const int k = k0 + 8 * s;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (v < Pipe<MT, CHECK>::AVEC && r < R && (!CHECK || k < K))
+      val = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
+    P.ar[J][q] = val;
+  }
+}
+
+template <int J, int MT, bool CHECK>
+__device__ __forceinline__ void pipe_stash(Pipe<MT, CHECK>& P, int st, int nst, bf16_t* As) {
+  if (st >= nst) return;
+  bf16_t* dst = As + (st & 1) * (XG_BM * XG_LDA);
+#pragma unroll
+  for (int q = 0; q < Pipe<MT, CHECK>::AV; ++q) {
+    const int v = threadIdx.x + 256 * q;
+    if (v < Pipe<MT, CHECK>::AVEC) {
+      const int r = v >> 3, s = v & 7;
+      *reinterpret_cast<u32x4*>(dst + r * XG_LDA + 8 * s) = P.ar[J][q];
+    }
+  }
+}
+
+template <int J, int MT, bool CHECK>
+__device__ __forceinline__ void pipe_compute(Pipe<MT, CHECK>& P, int st, const bf16_t* As,
+                                             f32x4 (&acc)[MT][4]) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const bf16_t* src = As + (st & 1) * (XG_BM * XG_LDA) + i * XG_LDA + 8 * g;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    bf16x8 bf[4];
+    transpose_b(P.b[J][sub], bf);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(src + 16 * mt * XG_LDA + 32 * sub);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16(af, bf[c], acc[mt][c]);
+    }
+  }
+}
+
+// Stage st uses ring slot J; it first refills slot J-1 (consumed by stage
+// st-1) with stage st+2, computes, then writes A of stage st+1 into LDS.
+template <int J, int MT, bool CHECK>
+__device__ __forceinline__ void pipe_step(Pipe<MT, CHECK>& P, int st, int nst,
+                                          const bf16_t* __restrict__ Ablk, int R,
+                                          const bf16_t* __restrict__ Bl, int K, int N, int col,
+                                          bf16_t* As, f32x4 (&acc)[MT][4]) {
+  if (st >= nst) return;
+  pipe_issue<(J + 2) % XG_NBUF>(P, st + 2, nst, Ablk, R, Bl, K, N, col);
+  pipe_compute<J>(P, st, As, acc);
+  pipe_stash<(J + 1) % XG_NBUF>(P, st + 1, nst, As);
+  __syncthreads();
+}
+
+template <bool SWIGLU, int MT, bool CHECK>
 __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bl,
                                           int K, int N, int col, bf16_t* __restrict__ C,
                                           const RowBlock& rb, bf16_t* As) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const int rows_tile = 16 * MT;
   const bf16_t* Ablk = A + (int64_t)rb.r0 * K;
+  const int nst = (K + XG_KS - 1) / XG_KS;
 
   f32x4 acc[MT][4];
 #pragma unroll
@@ -98,40 +191,19 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < K; k0 += XG_KS) {
-    BRaw br0, br1;
-    load_b_block(br0, Bl, N, k0, K, col, N);
-    load_b_block(br1, Bl, N, k0 + 32, K, col, N);
-    __syncthreads();  // previous stage fully consumed
-    for (int v = tid; v < rows_tile * (XG_KS / 8); v += 256) {
-      const int r = v >> 3, s = v & 7;
-      const int k = k0 + 8 * s;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (r < rb.R && k < K) val = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
-      *reinterpret_cast<u32x4*>(As + r * XG_LDA + 8 * s) = val;
-    }
-    __syncthreads();
-    bf16x8 bf[4];
-    transpose_b(br0, bf);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + (16 * mt + i) * XG_LDA + 8 * g);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16(af, bf[c], acc[mt][c]);
-    }
-    transpose_b(br1, bf);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(As + (16 * mt + i) * XG_LDA + 32 + 8 * g);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16(af, bf[c], acc[mt][c]);
-    }
+  Pipe<MT, CHECK> P;
+  pipe_issue<0>(P, 0, nst, Ablk, rb.R, Bl, K, N, col);
+  pipe_issue<1>(P, 1, nst, Ablk, rb.R, Bl, K, N, col);
+  pipe_stash<0>(P, 0, nst, As);
+  __syncthreads();
+  for (int st = 0; st < nst; st += XG_NBUF) {
+    pipe_step<0>(P, st, nst, Ablk, rb.R, Bl, K, N, col, As, acc);
+    pipe_step<1>(P, st + 1, nst, Ablk, rb.R, Bl, K, N, col, As, acc);
+    pipe_step<2>(P, st + 2, nst, Ablk, rb.R, Bl, K, N, col, As, acc);
   }
 
   // epilogue: lane holds 4 consecutive columns (c = 0..3) of rows 16 mt + 4 g + r
   const bool store_lane = SWIGLU ? (i < 8) : true;
-  const int ocol = SWIGLU ? col : col;  // output column of element c = 0
-  const int ldc = SWIGLU ? N : N;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -141,16 +213,16 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
       for (int c = 0; c < 4; ++c) {
         const float a = acc[mt][c][r];
         if (SWIGLU) {
-          const float b = __shfl_xor(a, 8);
+          const float b = __shfl_xor(a, 8);  // the W3 product of the same element
           o[c] = a / (1.0f + expf(-a)) * b;
         } else {
           o[c] = a;
         }
       }
       const int row = 16 * mt + 4 * g + r;
-      if (store_lane && row < rb.R && ocol < N) {
+      if (store_lane && row < rb.R && col < N) {
         u32x2 pk = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * ldc + ocol) = pk;
+        *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * N + col) = pk;
       }
     }
   }
@@ -158,7 +230,9 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
 
 // SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]; 128 columns per WG.
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d];  256 columns per WG.
-template <bool SWIGLU>
+// CHECK:  bounds checks on K and N (needed unless K % 64 == 0 and the column
+//         blocks tile N exactly).
+template <bool SWIGLU, bool CHECK>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
                                                          const int32_t* __restrict__ offsets,
                                                          int e_begin, int e_end,
@@ -166,11 +240,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16(const bf16_t* __restric
                                                          const bf16_t* __restrict__ B3, int K,
                                                          int N, bf16_t* __restrict__ C,
                                                          int nblk_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[XG_BM * XG_LDA];
-  __shared__ int sh[4];
-  const int mb = blockIdx.x / nblk_n;
-  const int nb = blockIdx.x - mb * nblk_n;
-  const RowBlock rb = find_row_block(offsets, e_begin, e_end, mb, sh);
+  __shared__ __attribute__((aligned(16))) bf16_t As[2 * XG_BM * XG_LDA];
+  __shared__ int pre[XG_MAXN + 1];
+  const RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, pre);
   if (rb.R <= 0) return;
   const int wave = threadIdx.x >> 6;
   const int i = threadIdx.x & 15;
@@ -178,16 +250,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16(const bf16_t* __restric
   const bf16_t* Bl;
   const int64_t estride = (int64_t)K * N;
   if (SWIGLU) {
-    col = nb * 128 + wave * 32 + 4 * (i & 7);
+    col = rb.nb * 128 + wave * 32 + 4 * (i & 7);
     Bl = ((i < 8) ? B1 : B3) + rb.e * estride;
   } else {
-    col = nb * 256 + wave * 64 + 4 * i;
+    col = rb.nb * 256 + wave * 64 + 4 * i;
     Bl = B1 + rb.e * estride;
   }
   const int mt = (rb.R + 15) >> 4;
   switch (mt) {
 #define XG_CASE(n) \
-  case n: gemm_body<SWIGLU, n>(A, Bl, K, N, col, C, rb, As); break;
+  case n: gemm_body<SWIGLU, n, CHECK>(A, Bl, K, N, col, C, rb, As); break;
     XG_CASE(1) XG_CASE(2) XG_CASE(3) XG_CASE(4) XG_CASE(5)
     XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
 #undef XG_CASE
@@ -233,13 +305,17 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
   if (p.dtype == 1) {
     const int64_t mblocks = (p.rows_max + XG_BM - 1) / XG_BM + (e_end - e_begin);
     const int nb1 = (p.f + 127) / 128;
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3((unsigned)(mblocks * nb1)), dim3(256), 0, st,
+    const bool chk1 = (p.d % XG_KS) != 0 || (p.f % 128) != 0;
+    auto k1 = chk1 ? grouped_gemm_bf16<true, true> : grouped_gemm_bf16<true, false>;
+    hipLaunchKernelGGL(k1, dim3((unsigned)(mblocks * nb1)), dim3(256), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
                        (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, nb1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nb2 = (p.d + 255) / 256;
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3((unsigned)(mblocks * nb2)), dim3(256), 0, st,
+    const bool chk2 = (p.f % XG_KS) != 0 || (p.d % 256) != 0;
+    auto k2 = chk2 ? grouped_gemm_bf16<false, true> : grouped_gemm_bf16<false, false>;
+    hipLaunchKernelGGL(k2, dim3((unsigned)(mblocks * nb2)), dim3(256), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
                        (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, nb2);
     return hipGetLastError();
