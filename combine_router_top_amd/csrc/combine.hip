@@ -4,14 +4,16 @@
 // ("CUCo: An Agentic Framework for Compute and Communication Co-design",
 // Table 4, row "MoE Dispatch/Combine").
 //
-// One wave per token.  Lanes 0..k-1 fetch the slot indices and weights once;
-// each lane then owns 16-byte column pieces of the row and reads the k source
-// rows' pieces (all issued before the multiply-adds), so every load and store
-// is a coalesced 16-byte access.
+// One wave per token.  Lanes 0..k-1 fetch the slot indices and weights once
+// and the wave compacts its local slots (in slot order) into LDS; each lane
+// then owns 16-byte column pieces of the row, four of them in flight per
+// source row, so every load and store is a coalesced 16-byte access.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+constexpr int CB_U = 4;  // 16-byte pieces per lane in flight per source row
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ yp,
@@ -19,8 +21,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
                                                       const float* __restrict__ w,
                                                       u32x4* __restrict__ y, int T, int k,
                                                       int nvec) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ int s_row[4][32];
+  __shared__ float s_w[4][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   int my_row = -1;
   float my_w = 0.f;
@@ -28,55 +32,63 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     my_row = inv[(int64_t)t * k + lane];
     my_w = w[(int64_t)t * k + lane];
   }
-  // compact the local slots, keeping slot order
+  // compact the local slots into LDS, keeping slot order
   const uint64_t valid = __ballot(my_row >= 0);
   const int nloc = __popcll(valid);
+  if (my_row >= 0) {
+    const int at = __popcll(valid & lanemask_lt());
+    s_row[wave][at] = my_row;
+    s_w[wave][at] = my_w;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int NQ = BF16 ? 8 : 4;
   u32x4* dst = y + (int64_t)t * nvec;
-  for (int v = lane; v < nvec; v += 64) {
-    float acc[BF16 ? 8 : 4];
+  for (int v0 = lane; v0 < nvec; v0 += 64 * CB_U) {
+    float acc[CB_U][NQ];
 #pragma unroll
-    for (int q = 0; q < (BF16 ? 8 : 4); ++q) acc[q] = 0.f;
-    uint64_t rest = valid;
-    for (int j0 = 0; j0 < nloc; j0 += 4) {
-      u32x4 val[4];
-      float wj[4];
+    for (int u = 0; u < CB_U; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wj[u] = 0.f;
-        val[u] = u32x4{0u, 0u, 0u, 0u};
-        if (j0 + u < nloc) {
-          const int src = __ffsll((unsigned long long)rest) - 1;
-          rest &= rest - 1;
-          const int row = __shfl(my_row, src);
-          wj[u] = __shfl(my_w, src);
-          val[u] = yp[(int64_t)row * nvec + v];
-        }
+      for (int q = 0; q < NQ; ++q) acc[u][q] = 0.f;
+    for (int j = 0; j < nloc; ++j) {
+      const int row = s_row[wave][j];
+      const float wj = s_w[wave][j];
+      const u32x4* src = yp + (int64_t)row * nvec;
+      u32x4 val[CB_U];
+#pragma unroll
+      for (int u = 0; u < CB_U; ++u) {
+        const int v = v0 + 64 * u;
+        val[u] = v < nvec ? src[v] : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (j0 + u < nloc) {
-          if (BF16) {
+      for (int u = 0; u < CB_U; ++u) {
+        if (BF16) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              acc[2 * q] = fmaf(wj[u], bf16_lo(val[u][q]), acc[2 * q]);
-              acc[2 * q + 1] = fmaf(wj[u], bf16_hi(val[u][q]), acc[2 * q + 1]);
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj[u], __uint_as_float(val[u][q]), acc[q]);
+          for (int q = 0; q < 4; ++q) {
+            acc[u][2 * q] = fmaf(wj, bf16_lo(val[u][q]), acc[u][2 * q]);
+            acc[u][2 * q + 1] = fmaf(wj, bf16_hi(val[u][q]), acc[u][2 * q + 1]);
           }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[u][q] = fmaf(wj, __uint_as_float(val[u][q]), acc[u][q]);
         }
       }
     }
-    u32x4 o;
-    if (BF16) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    } else {
+    for (int u = 0; u < CB_U; ++u) {
+      const int v = v0 + 64 * u;
+      if (v >= nvec) continue;
+      u32x4 o;
+      if (BF16) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[u][q]);
+      }
+      dst[v] = o;
     }
-    dst[v] = o;
   }
 }
 

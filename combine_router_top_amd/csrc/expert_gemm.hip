@@ -26,15 +26,12 @@
 // fp32 problems only.
 #include "common.h"
 #include "kernels.h"
-#include "mfma_tile.h"
+#include "gemm_core.h"
 
 namespace moe {
 
 constexpr int XG_MTMAX = 10;              // m-tiles per row block
 constexpr int XG_BM = 16 * XG_MTMAX;      // rows per row block
-constexpr int XG_KS = 64;                 // K per pipeline stage
-constexpr int XG_LDA = XG_KS + 8;         // LDS row stride (bf16): 144 B, conflict-free fragment reads
-constexpr int XG_NBUF = 3;                // register ring: stage being computed + 2 in flight
 constexpr int XG_MAXN = 1024;             // max local experts
 
 // Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb.
@@ -93,114 +90,15 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   return rb;
 }
 
-// One pipeline stage = 64 of K.  Per stage each lane loads its two 8x4 weight
-// blocks (B) and its share of the A tile (A rows x 64 k) into register ring
-// slot J; the A share is later written to the LDS double buffer.
-template <int MT, bool CHECK>
-struct Pipe {
-  static constexpr int AVEC = 16 * MT * (XG_KS / 8);  // 16-byte A vectors per stage
-  static constexpr int AV = (AVEC + 255) / 256;       // per thread
-  BRaw b[XG_NBUF][2];
-  u32x4 ar[XG_NBUF][AV];
-};
-
-template <int J, int MT, bool CHECK>
-__device__ __forceinline__ void pipe_issue(Pipe<MT, CHECK>& P, int st, int nst,
-                                           const bf16_t* __restrict__ Ablk, int R,
-                                           const bf16_t* __restrict__ Bl, int K, int N, int col) {
-  if (st >= nst) return;
-  const int k0 = st * XG_KS;
-  if (CHECK) {
-    load_b_block(P.b[J][0], Bl, N, k0, K, col, N);
-    load_b_block(P.b[J][1], Bl, N, k0 + 32, K, col, N);
-  } else {
-    load_b_block_nocheck(P.b[J][0], Bl, N, k0, col);
-    load_b_block_nocheck(P.b[J][1], Bl, N, k0 + 32, col);
-  }
-#pragma unroll
-  for (int q = 0; q < Pipe<MT, CHECK>::AV; ++q) {
-    const int v = threadIdx.x + 256 * q;
-    const int r = v >> 3, s = v & 7;
-    const int k = k0 + 8 * s;
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (v < Pipe<MT, CHECK>::AVEC && r < R && (!CHECK || k < K))
-      val = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
-    P.ar[J][q] = val;
-  }
-}
-
-template <int J, int MT, bool CHECK>
-__device__ __forceinline__ void pipe_stash(Pipe<MT, CHECK>& P, int st, int nst, bf16_t* As) {
-  if (st >= nst) return;
-  bf16_t* dst = As + (st & 1) * (XG_BM * XG_LDA);
-#pragma unroll
-  for (int q = 0; q < Pipe<MT, CHECK>::AV; ++q) {
-    const int v = threadIdx.x + 256 * q;
-    if (v < Pipe<MT, CHECK>::AVEC) {
-      const int r = v >> 3, s = v & 7;
-      *reinterpret_cast<u32x4*>(dst + r * XG_LDA + 8 * s) = P.ar[J][q];
-    }
-  }
-}
-
-template <int J, int MT, bool CHECK>
-__device__ __forceinline__ void pipe_compute(Pipe<MT, CHECK>& P, int st, const bf16_t* As,
-                                             f32x4 (&acc)[MT][4]) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, g = lane >> 4;
-  const bf16_t* src = As + (st & 1) * (XG_BM * XG_LDA) + i * XG_LDA + 8 * g;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    bf16x8 bf[4];
-    transpose_b(P.b[J][sub], bf);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(src + 16 * mt * XG_LDA + 32 * sub);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16(af, bf[c], acc[mt][c]);
-    }
-  }
-}
-
-// Stage st uses ring slot J; it first refills slot J-1 (consumed by stage
-// st-1) with stage st+2, computes, then writes A of stage st+1 into LDS.
-template <int J, int MT, bool CHECK>
-__device__ __forceinline__ void pipe_step(Pipe<MT, CHECK>& P, int st, int nst,
-                                          const bf16_t* __restrict__ Ablk, int R,
-                                          const bf16_t* __restrict__ Bl, int K, int N, int col,
-                                          bf16_t* As, f32x4 (&acc)[MT][4]) {
-  if (st >= nst) return;
-  pipe_issue<(J + 2) % XG_NBUF>(P, st + 2, nst, Ablk, R, Bl, K, N, col);
-  pipe_compute<J>(P, st, As, acc);
-  pipe_stash<(J + 1) % XG_NBUF>(P, st + 1, nst, As);
-  __syncthreads();
-}
-
 template <bool SWIGLU, int MT, bool CHECK>
 __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bl,
                                           int K, int N, int col, bf16_t* __restrict__ C,
                                           const RowBlock& rb, bf16_t* As) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const bf16_t* Ablk = A + (int64_t)rb.r0 * K;
-  const int nst = (K + XG_KS - 1) / XG_KS;
-
+  GemmArgs ga{A + (int64_t)rb.r0 * K, K, rb.R, Bl, N, 0, K, N, col};
   f32x4 acc[MT][4];
-#pragma unroll
-  for (int a = 0; a < MT; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  Pipe<MT, CHECK> P;
-  pipe_issue<0>(P, 0, nst, Ablk, rb.R, Bl, K, N, col);
-  pipe_issue<1>(P, 1, nst, Ablk, rb.R, Bl, K, N, col);
-  pipe_stash<0>(P, 0, nst, As);
-  __syncthreads();
-  for (int st = 0; st < nst; st += XG_NBUF) {
-    pipe_step<0>(P, st, nst, Ablk, rb.R, Bl, K, N, col, As, acc);
-    pipe_step<1>(P, st + 1, nst, Ablk, rb.R, Bl, K, N, col, As, acc);
-    pipe_step<2>(P, st + 2, nst, Ablk, rb.R, Bl, K, N, col, As, acc);
-  }
+  gemm_mainloop<MT, CHECK>(ga, As, acc);
 
   // epilogue: lane holds 4 consecutive columns (c = 0..3) of rows 16 mt + 4 g + r
   const bool store_lane = SWIGLU ? (i < 8) : true;
@@ -240,7 +138,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16(const bf16_t* __restric
                                                          const bf16_t* __restrict__ B3, int K,
                                                          int N, bf16_t* __restrict__ C,
                                                          int nblk_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2 * XG_BM * XG_LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t As[2 * XG_BM * GC_LDA];
   __shared__ int pre[XG_MAXN + 1];
   const RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, pre);
   if (rb.R <= 0) return;
@@ -305,7 +203,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
   if (p.dtype == 1) {
     const int64_t mblocks = (p.rows_max + XG_BM - 1) / XG_BM + (e_end - e_begin);
     const int nb1 = (p.f + 127) / 128;
-    const bool chk1 = (p.d % XG_KS) != 0 || (p.f % 128) != 0;
+    const bool chk1 = (p.d % GC_KS) != 0 || (p.f % 128) != 0;
     auto k1 = chk1 ? grouped_gemm_bf16<true, true> : grouped_gemm_bf16<true, false>;
     hipLaunchKernelGGL(k1, dim3((unsigned)(mblocks * nb1)), dim3(256), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
@@ -313,7 +211,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nb2 = (p.d + 255) / 256;
-    const bool chk2 = (p.f % XG_KS) != 0 || (p.d % 256) != 0;
+    const bool chk2 = (p.f % GC_KS) != 0 || (p.d % 256) != 0;
     auto k2 = chk2 ? grouped_gemm_bf16<false, true> : grouped_gemm_bf16<false, false>;
     hipLaunchKernelGGL(k2, dim3((unsigned)(mblocks * nb2)), dim3(256), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,

@@ -6,11 +6,10 @@
 // lower expert index.
 //
 // Kernels
-//   router_wide_mfma    bf16, E % 4 == 0 and E > 16: split-K MFMA GEMM, each
-//                       wave owns 64 expert columns, the workgroup 64 tokens
-//                       and 256 experts; A (x rows) staged through LDS, B
-//                       (W_g) transposed in registers.  Writes fp32 partial
-//                       sums per K split.
+//   router_wide_mfma    bf16, E % 4 == 0 and E > 16: split-K MFMA GEMM on the
+//                       pipelined core (gemm_core.h); each wave owns 64
+//                       expert columns, the workgroup 64 tokens and 256
+//                       experts.  Writes fp32 partial sums per K split.
 //   router_narrow_mfma  bf16, E <= 16 and E*d <= 32K: W_g^T staged once in LDS,
 //                       each wave streams its own 32 token rows straight from
 //                       HBM into MFMA A fragments.  HBM-bound on x.
@@ -20,79 +19,44 @@
 //                       adds the bias, optionally stores the logits, then k
 //                       rounds of a wave-wide max over (value, index) keys.
 #include "common.h"
-#include "mfma_tile.h"
+#include "gemm_core.h"
 #include "kernels.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// wide router (bf16, MFMA, split-K)
+// wide router (bf16, MFMA, split-K) on the pipelined core of gemm_core.h
 // ---------------------------------------------------------------------------
-constexpr int RW_BM = 64;       // tokens per workgroup (4 m-tiles)
+constexpr int RW_MT = 4;        // m-tiles per workgroup
+constexpr int RW_BM = 16 * RW_MT;  // tokens per workgroup
 constexpr int RW_BN = 256;      // experts per workgroup (4 waves x 64)
-constexpr int RW_KS = 64;       // K per LDS stage
-constexpr int RW_LDA = RW_KS + 8;  // LDS row stride in bf16 (16-byte pad)
 
+template <bool CHECK>
 __global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict__ x,
                                                         const bf16_t* __restrict__ wg,
                                                         float* __restrict__ part, int T, int d,
                                                         int E, int kchunk) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[RW_BM * RW_LDA];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2 * RW_BM * GC_LDA];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int m0 = blockIdx.x * RW_BM;
   const int split = blockIdx.y;
   const int kbeg = split * kchunk;
   const int kend = min(d, kbeg + kchunk);
-  const int nc = blockIdx.z * RW_BN + wave * 64 + 4 * i;  // this lane's 4 columns
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = kbeg; k0 < kend; k0 += RW_KS) {
-    // stage A: 64 rows x 64 k, 16 bytes per thread per pass (2 passes)
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int v = tid + pass * 256;
-      const int r = v >> 3, s = v & 7;
-      const int row = m0 + r, k = k0 + 8 * s;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (row < T && k < kend) val = *reinterpret_cast<const u32x4*>(x + (int64_t)row * d + k);
-      *reinterpret_cast<u32x4*>(As + r * RW_LDA + 8 * s) = val;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kb = k0 + 32 * sub;
-      BRaw br;
-      load_b_block(br, wg, E, kb, kend, nc, E);
-      bf16x8 bf[4];
-      transpose_b(br, bf);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 af =
-            *reinterpret_cast<const bf16x8*>(As + (16 * mt + i) * RW_LDA + 32 * sub + 8 * g);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[mt][c] = mfma16(af, bf[c], acc[mt][c]);
-      }
-    }
-    __syncthreads();
-  }
-  if (nc >= E) return;
+  const int col = blockIdx.z * RW_BN + wave * 64 + 4 * i;
+  GemmArgs ga{x + (int64_t)m0 * d, d, min(RW_BM, T - m0), wg, E, kbeg, kend, E, col};
+  f32x4 acc[RW_MT][4];
+  gemm_mainloop<RW_MT, CHECK>(ga, As, acc);
+  if (col >= E) return;
   float* out = part + (int64_t)split * T * E;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < RW_MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = m0 + 16 * mt + 4 * g + r;
       if (row < T) {
         f32x4 v = f32x4{acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
-        *reinterpret_cast<f32x4*>(out + (int64_t)row * E + nc) = v;
+        *reinterpret_cast<f32x4*>(out + (int64_t)row * E + col) = v;
       }
     }
 }
@@ -181,21 +145,45 @@ __global__ __launch_bounds__(256) void router_plain(const TIn* __restrict__ x,
 // ---------------------------------------------------------------------------
 // top-k + renormalised softmax: one wave per token
 // ---------------------------------------------------------------------------
+// 64-bit keys: order-preserving fp32 bits in the high word, (1023 - expert) in
+// the low word, so the maximum key is the largest logit with ties resolved to
+// the lower expert index.  A logit key is never 0, so 0 marks "taken/absent".
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wave, returned uniformly: butterfly inside each 16-lane row
+// with DPP (quad swaps, half-row mirror, row mirror), then the four row maxima
+// through readlane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp_u64<0xB1>(v));   // quad_perm 1,0,3,2
+  v = umax64(v, dpp_u64<0x4E>(v));   // quad_perm 2,3,0,1
+  v = umax64(v, dpp_u64<0x141>(v));  // row_half_mirror
+  v = umax64(v, dpp_u64<0x140>(v));  // row_mirror
+  uint64_t m = 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 16 * r);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 16 * r);
+    m = umax64(m, ((uint64_t)hi << 32) | lo);
   }
-  return v;
+  return m;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0xB1, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x4E, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x141, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0u, __builtin_bit_cast(uint32_t, v), 0x140, 0xf, 0xf, false));
+  float s = 0.f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  for (int r = 0; r < 4; ++r)
+    s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(uint32_t, v), 16 * r));
+  return s;
 }
 
 __device__ __forceinline__ float key_to_f32(uint32_t ok) {
@@ -203,8 +191,8 @@ __device__ __forceinline__ float key_to_f32(uint32_t ok) {
   return __uint_as_float(u);
 }
 
-constexpr int TK_MAXV = 16;  // E <= 1024 = 16 values per lane
-
+// NV = values per lane = ceil(E / 64).
+template <int NV>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ part,
                                                            int nsplit, const float* __restrict__ bias,
                                                            float* __restrict__ logits_out, int T,
@@ -213,13 +201,12 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int nv = (E + 63) >> 6;
-  uint64_t key[TK_MAXV];
+  uint64_t key[NV];
 #pragma unroll
-  for (int j = 0; j < TK_MAXV; ++j) {
+  for (int j = 0; j < NV; ++j) {
     key[j] = 0;
     const int e = lane + 64 * j;
-    if (j < nv && e < E) {
+    if (e < E) {
       float v = part[(int64_t)t * E + e];
       for (int s = 1; s < nsplit; ++s) v += part[((int64_t)s * T + t) * E + e];
       if (bias) v += bias[e];
@@ -227,13 +214,12 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
       key[j] = ((uint64_t)f32_order_key(v) << 32) | (uint32_t)(1023 - e);
     }
   }
-  float myv = 0.f;
+  float myv = 0.f, v0 = 0.f;
   int mye = 0;
-  float v0 = 0.f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int j = 0; j < TK_MAXV; ++j) best = key[j] > best ? key[j] : best;
+    for (int j = 1; j < NV; ++j) best = umax64(best, key[j]);
     best = wave_max_u64(best);
     const int e = 1023 - (int)(uint32_t)(best & 0xFFFFFFFFu);
     const float v = key_to_f32((uint32_t)(best >> 32));
@@ -242,10 +228,9 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
       myv = v;
       mye = e;
     }
-    // remove the winner from its owner lane
     if ((e & 63) == lane) {
 #pragma unroll
-      for (int j = 0; j < TK_MAXV; ++j)
+      for (int j = 0; j < NV; ++j)
         if (j == (e >> 6)) key[j] = 0;
     }
   }
@@ -270,12 +255,17 @@ static RouteKind route_kind(const Prob& p) {
 
 static int route_splits(const Prob& p) {
   if (route_kind(p) != ROUTE_WIDE) return 1;
-  // enough workgroups to cover the chip; every split keeps >= 512 of K
-  const int64_t mblocks = (p.T + RW_BM - 1) / RW_BM;
-  const int64_t nblocks = (p.E + RW_BN - 1) / RW_BN;
-  int s = 1;
-  while (mblocks * nblocks * s < 256 && p.d / (2 * s) >= 512) s *= 2;
-  return s;
+  // enough workgroups to cover the chip, every split keeps >= 256 of K
+  const int64_t blocks = (int64_t)((p.T + RW_BM - 1) / RW_BM) * ((p.E + RW_BN - 1) / RW_BN);
+  int64_t s = (256 + blocks - 1) / blocks;
+  const int64_t smax = p.d / 256 > 1 ? p.d / 256 : 1;
+  if (s > smax) s = smax;
+  return (int)s;
+}
+
+static int route_kchunk(const Prob& p, int S) {
+  const int kc = (p.d + S - 1) / S;
+  return (kc + GC_KS - 1) / GC_KS * GC_KS;
 }
 
 size_t route_ws_bytes(const Prob& p) {
@@ -289,11 +279,12 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
   const RouteKind kind = route_kind(p);
   const int S = route_splits(p);
   if (kind == ROUTE_WIDE) {
-    int kchunk = (p.d + S - 1) / S;
-    kchunk = (kchunk + RW_KS - 1) / RW_KS * RW_KS;
+    const int kchunk = route_kchunk(p, S);
+    const bool check = (p.E % RW_BN) != 0 || (p.d % GC_KS) != 0;
     dim3 grid((p.T + RW_BM - 1) / RW_BM, S, (p.E + RW_BN - 1) / RW_BN);
-    hipLaunchKernelGGL(router_wide_mfma, grid, dim3(256), 0, st, (const bf16_t*)x,
-                       (const bf16_t*)wg, part, p.T, p.d, p.E, kchunk);
+    auto kern = check ? router_wide_mfma<true> : router_wide_mfma<false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wg, part, p.T,
+                       p.d, p.E, kchunk);
   } else if (kind == ROUTE_NARROW) {
     dim3 grid((p.T + RN_ROWS - 1) / RN_ROWS);
     const size_t lds = (size_t)p.E * p.d * sizeof(bf16_t);
@@ -311,8 +302,14 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_softmax_kernel, dim3((p.T + 3) / 4), dim3(256), 0, st, part, S, bias,
-                     logits, p.T, p.E, p.k, idx, w);
+  const int nv = (p.E + 63) / 64;
+  auto tk = nv <= 1 ? topk_softmax_kernel<1>
+          : nv <= 2 ? topk_softmax_kernel<2>
+          : nv <= 4 ? topk_softmax_kernel<4>
+          : nv <= 8 ? topk_softmax_kernel<8>
+                    : topk_softmax_kernel<16>;
+  hipLaunchKernelGGL(tk, dim3((p.T + 3) / 4), dim3(256), 0, st, part, S, bias, logits, p.T, p.E,
+                     p.k, idx, w);
   return hipGetLastError();
 }
 
