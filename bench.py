@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--overlap", action="store_true", help="two-stream dispatch overlap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--copy-gib", type=float, default=1.0,
+                    help="size of the device-to-device copy that measures practical HBM bandwidth")
     return ap.parse_args()
 
 
@@ -93,6 +95,29 @@ def roofline(bytes_, flops, sec, dtype):
     ach = bytes_ / sec / 1e9
     peak = HBM_PEAK / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": peak, "unit": "GB/s", "frac": ach / peak}
+
+
+def copy_bandwidth(gib, reps=5):
+    """Device-to-device copy of `gib` GiB (read + write counted): the practical
+    HBM ceiling for context, and the known-size kernel that calibrates the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": 2 * n, "gbs": 2 * n / sec / 1e9, "us": sec * 1e6}
 
 
 def cpu_baseline(w, inp, budget):
@@ -152,6 +177,7 @@ def main():
         return torch.from_numpy(x).cuda()
 
     torch.cuda.set_device(0)
+    copy = copy_bandwidth(a.copy_gib) if a.copy_gib > 0 else None
     d = {k: dev(v) for k, v in inp.items()}
     p = M.Spec.of(w, M.MOE_F_OVERLAP if a.overlap else 0)
     stream = torch.cuda.current_stream()
@@ -251,6 +277,7 @@ def main():
         "roofline": roof,
         "phases": phases,
         "wall_ms_per_step": wall / a.steps * 1e3,
+        "hbm_copy": copy,
         "input_gen_s": gen_s,
     }
     if not a.no_cpu_baseline:

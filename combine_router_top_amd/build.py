@@ -41,9 +41,9 @@ def device_flags():
     return ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
 
 
-def compile_one(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + common_flags()
+def compile_one(src: str, defs=(), build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + common_flags() + ["-D" + d for d in defs]
     if src.endswith(".hip"):
         cmd += device_flags()
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,26 +56,33 @@ def compile_one(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = True, defs=(), lib: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile and link.  ``defs`` are extra preprocessor definitions (tile-shape
+    tuning knobs such as MOE_XG_NW=4); ``lib``/``build_dir`` redirect the output."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: compile_one(s, defs, build_dir), SOURCES))
+    LIB_OUT = lib
+    tmp = LIB_OUT + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, LIB_OUT)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {LIB_OUT}")
+    return LIB_OUT
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
+    ap.add_argument("-D", dest="defs", action="append", default=[])
+    ap.add_argument("--lib", default=LIB)
+    ap.add_argument("--build-dir", default=BUILD)
     a = ap.parse_args()
-    build(a.jobs)
+    build(a.jobs, defs=a.defs, lib=a.lib, build_dir=a.build_dir)
 
 
 if __name__ == "__main__":

@@ -10,9 +10,10 @@
 // expert (up to 160 rows) and one column block; every weight byte of that
 // column block is streamed from HBM exactly once per row block, which is the
 // bound for the segment sizes of a sparse MoE layer (about 4..160 rows per
-// expert).  A rows are staged through LDS (shared by the 4 waves); weights go
-// straight from HBM into registers and are transposed there into MFMA B
-// fragments (see mfma_tile.h).  The row-block schedule is derived on the
+// expert).  8 waves (2 per SIMD) share the A rows through LDS; each wave
+// streams its own weight columns (2 per lane) straight from HBM into
+// registers and transposes them there into MFMA B fragments (mfma_tile.h,
+// gemm_core.h).  The row-block schedule is derived on the
 // device from `offsets` in the workgroup prologue, so the number of local
 // assignments never travels to the host; the grid is sized for the worst case
 // and surplus workgroups exit after the prologue.
@@ -24,6 +25,8 @@
 //
 // fp32 path (grouped_gemm_f32): one thread per output element, for the small
 // fp32 problems only.
+#include <stdint.h>
+
 #include "common.h"
 #include "kernels.h"
 #include "gemm_core.h"
@@ -32,6 +35,18 @@ namespace moe {
 
 constexpr int XG_MTMAX = 10;              // m-tiles per row block
 constexpr int XG_BM = 16 * XG_MTMAX;      // rows per row block
+// Build-time tile shape (a tuning choice, not a behaviour switch).
+#ifndef MOE_XG_NW
+#define MOE_XG_NW 8
+#endif
+#ifndef MOE_XG_CPL
+#define MOE_XG_CPL 2
+#endif
+constexpr int XG_NW = MOE_XG_NW;          // waves per workgroup
+constexpr int XG_CPL = MOE_XG_CPL;        // weight columns per lane (2: 4-byte loads, 4: 8-byte)
+constexpr int XG_HW = 128 / XG_NW;        // h columns per wave in GEMM-1 (128 per workgroup)
+constexpr int XG_OW = 256 / XG_NW;        // output columns per wave in GEMM-2 (256 per workgroup)
+static_assert(XG_HW == 8 * XG_CPL && XG_OW == 16 * XG_CPL, "tile shape");
 constexpr int XG_MAXN = 1024;             // max local experts
 
 // Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb.
@@ -46,7 +61,7 @@ struct RowBlock {
 // a contiguous range of (row block, column block) pairs: all column blocks of
 // one row block then share one L2 for their A rows.  R = 0 means "exit".
 __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, int e_end,
-                             int nblk_n, int* pre) {
+                             int nblk_n, int th, int* pre) {
   const int ne = e_end - e_begin;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -54,7 +69,7 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
     for (int j0 = 0; j0 < ne; j0 += 64) {
       const int j = j0 + lane;
       const int cnt = j < ne ? offsets[e_begin + j + 1] - offsets[e_begin + j] : 0;
-      const int nb = (cnt + XG_BM - 1) / XG_BM;
+      const int nb = cnt < th ? (cnt + XG_BM - 1) / XG_BM : 0;
       int x = nb;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -97,18 +112,18 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   GemmArgs ga{A + (int64_t)rb.r0 * K, K, rb.R, Bl, N, 0, K, N, col};
-  f32x4 acc[MT][4];
-  gemm_mainloop<MT, CHECK>(ga, As, acc);
+  f32x4 acc[MT][XG_CPL];
+  gemm_mainloop<XG_NW, XG_CPL, MT, CHECK>(ga, As, acc);
 
-  // epilogue: lane holds 4 consecutive columns (c = 0..3) of rows 16 mt + 4 g + r
+  // epilogue: lane holds XG_CPL consecutive columns (c) of rows 16 mt + 4 g + r
   const bool store_lane = SWIGLU ? (i < 8) : true;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float o[4];
+      float o[XG_CPL];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < XG_CPL; ++c) {
         const float a = acc[mt][c][r];
         if (SWIGLU) {
           const float b = __shfl_xor(a, 8);  // the W3 product of the same element
@@ -119,8 +134,12 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
       }
       const int row = 16 * mt + 4 * g + r;
       if (store_lane && row < rb.R && col < N) {
-        u32x2 pk = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * N + col) = pk;
+        if (XG_CPL == 2) {
+          *reinterpret_cast<uint32_t*>(C + (int64_t)(rb.r0 + row) * N + col) = pack_bf16x2(o[0], o[1]);
+        } else {
+          *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * N + col) =
+              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[XG_CPL - 2], o[XG_CPL - 1])};
+        }
       }
     }
   }
@@ -131,27 +150,28 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
 // CHECK:  bounds checks on K and N (needed unless K % 64 == 0 and the column
 //         blocks tile N exactly).
 template <bool SWIGLU, bool CHECK>
-__global__ __launch_bounds__(256) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int e_begin, int e_end,
-                                                         const bf16_t* __restrict__ B1,
-                                                         const bf16_t* __restrict__ B3, int K,
-                                                         int N, bf16_t* __restrict__ C,
-                                                         int nblk_n) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2 * XG_BM * GC_LDA];
+__global__ __launch_bounds__(64 * XG_NW) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 int e_begin, int e_end,
+                                                                 const bf16_t* __restrict__ B1,
+                                                                 const bf16_t* __restrict__ B3,
+                                                                 int K, int N,
+                                                                 bf16_t* __restrict__ C,
+                                                                 int nblk_n, int th) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<XG_NW, XG_CPL, XG_MTMAX>()];
   __shared__ int pre[XG_MAXN + 1];
-  const RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, pre);
+  const RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, th, pre);
   if (rb.R <= 0) return;
   const int wave = threadIdx.x >> 6;
   const int i = threadIdx.x & 15;
   int col;
   const bf16_t* Bl;
   const int64_t estride = (int64_t)K * N;
-  if (SWIGLU) {
-    col = rb.nb * 128 + wave * 32 + 4 * (i & 7);
+  if (SWIGLU) {  // 16 h columns per wave: lanes 0..7 read W1, lanes 8..15 the same W3 columns
+    col = rb.nb * 128 + wave * XG_HW + XG_CPL * (i & 7);
     Bl = ((i < 8) ? B1 : B3) + rb.e * estride;
-  } else {
-    col = rb.nb * 256 + wave * 64 + 4 * i;
+  } else {       // 32 output columns per wave
+    col = rb.nb * 256 + wave * XG_OW + XG_CPL * i;
     Bl = B1 + rb.e * estride;
   }
   const int mt = (rb.R + 15) >> 4;
@@ -162,6 +182,251 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16(const bf16_t* __restric
     XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
 #undef XG_CASE
     default: break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// large segments: 256 x 256 tiles, both operands through LDS
+// ---------------------------------------------------------------------------
+// For experts with at least XB_TH rows the weight-streaming kernel above would
+// re-read the weights once per 160-row block; here a workgroup computes a
+// 256-row x 256-weight-column tile with 4 waves of 128 x 128 (accumulators in
+// AGPRs).  Per 64-K stage every thread loads 8 A vectors and one 8 x 8 weight
+// block into registers (the next stage is in flight while the current one is
+// multiplied), transposes the weight block and writes both into the other LDS
+// buffer.  Weight columns are placed in LDS so that each lane's 8 n-tiles are
+// 8 consecutive output columns (16-byte stores), and for GEMM-1 so that W1 and
+// W3 of one column meet in lanes i and i ^ 8.
+constexpr int XB_BM = 256;
+constexpr int XB_BN = 256;      // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
+constexpr int XB_TH = 320;      // row count from which an expert uses this kernel
+constexpr int XB_GM = 4;        // m-tiles grouped together along the XCD-local order
+
+struct BigTile {
+  int e, r0, R, nt;
+};
+
+__device__ BigTile schedule_big(const int32_t* __restrict__ offsets, int e_begin, int e_end,
+                                int ntn, int* pre) {
+  const int ne = e_end - e_begin;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int j0 = 0; j0 < ne; j0 += 64) {
+      const int j = j0 + lane;
+      const int cnt = j < ne ? offsets[e_begin + j + 1] - offsets[e_begin + j] : 0;
+      const int nb = cnt >= XB_TH ? (cnt + XB_BM - 1) / XB_BM : 0;
+      int x = nb;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      if (j < ne) pre[j] = carry + x;
+      carry += __shfl(x, 63);
+    }
+    if (lane == 0) pre[XG_MAXN] = carry;
+  }
+  __syncthreads();
+  BigTile bt{0, 0, 0, 0};
+  const int tot_m = pre[XG_MAXN];
+  const int G = tot_m * ntn;
+  const int b = blockIdx.x;
+  if (b >= G) return bt;
+  const int xcd = b & 7, q = b >> 3;
+  const int L = xcd * (G >> 3) + min(xcd, G & 7) + q;
+  // groups of XB_GM m-tiles; inside a group the m-tile index runs fastest
+  const int mg = L / (XB_GM * ntn);
+  const int rem = L - mg * XB_GM * ntn;
+  const int gsz = min(XB_GM, tot_m - mg * XB_GM);
+  bt.nt = rem / gsz;
+  const int mt = mg * XB_GM + (rem - bt.nt * gsz);
+  int lo = 0, hi = ne - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] > mt) hi = mid; else lo = mid + 1;
+  }
+  const int e = e_begin + lo;
+  const int jb = mt - (lo ? pre[lo - 1] : 0);
+  const int o = offsets[e];
+  bt.e = e;
+  bt.r0 = o + jb * XB_BM;
+  bt.R = min(XB_BM, offsets[e + 1] - o - jb * XB_BM);
+  return bt;
+}
+
+struct BigRegs {
+  u32x4 a[8];
+  u32x4 b[8];
+};
+
+template <bool SWIGLU, bool CHECK>
+__device__ __forceinline__ void big_load(BigRegs& R, const bf16_t* __restrict__ Ablk, int Rrows,
+                                         int K, const bf16_t* __restrict__ Bp, int N, int bcol,
+                                         int k0) {
+  // Rows past Rrows are clamped to the last valid row (finite values in rows
+  // that are never stored), so the unchecked path has no predicated loads.
+  const int t = threadIdx.x;
+  const int k = k0 + 8 * (t & 7);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = min((t >> 3) + 32 * j, Rrows - 1);
+    if (CHECK) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (k < K) v = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
+      R.a[j] = v;
+    } else {
+      R.a[j] = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
+    }
+  }
+  const int kb = t >> 5;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int kk = k0 + 8 * kb + r;
+    if (CHECK) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (kk < K && bcol < N) v = *reinterpret_cast<const u32x4*>(Bp + (int64_t)kk * N + bcol);
+      R.b[r] = v;
+    } else {
+      R.b[r] = *reinterpret_cast<const u32x4*>(Bp + (int64_t)kk * N + bcol);
+    }
+  }
+}
+
+// LDS row (within the 256-row B^T tile) of weight column c of this thread's block.
+template <bool SWIGLU>
+__device__ __forceinline__ int big_brow(int nb, int c) {
+  if (SWIGLU) {
+    const int m3 = nb >> 4;             // 0: W1, 1: W3
+    const int hc = 8 * (nb & 15) + c;   // h column within the tile (0..127)
+    const int wn = hc >> 6, hw = hc & 63;
+    return 128 * wn + 16 * (hw & 7) + 8 * m3 + (hw >> 3);
+  } else {
+    const int wc = 8 * nb + c;          // weight column within the tile (0..255)
+    const int wn = wc >> 7, cw = wc & 127;
+    return 128 * wn + 16 * (cw & 7) + (cw >> 3);
+  }
+}
+
+template <bool SWIGLU>
+__device__ __forceinline__ void big_store(const BigRegs& R, bf16_t* As, bf16_t* Bs) {
+  const int t = threadIdx.x;
+  const int s = t & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (t >> 3) + 32 * j;
+    *reinterpret_cast<u32x4*>(As + r * GC_LDA + 8 * s) = R.a[j];
+  }
+  const int kb = t >> 5, nb = t & 31;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = __builtin_amdgcn_perm(R.b[2 * q + 1][c >> 1], R.b[2 * q][c >> 1], sel);
+    *reinterpret_cast<u32x4*>(Bs + big_brow<SWIGLU>(nb, c) * GC_LDA + 8 * kb) = v;
+  }
+}
+
+__device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs,
+                                            f32x4 (&acc)[8][8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  const bf16_t* a0 = As + (128 * wm + i) * GC_LDA + 8 * g;
+  const bf16_t* b0 = Bs + (128 * wn + i) * GC_LDA + 8 * g;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    bf16x8 bf[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      bf[t] = *reinterpret_cast<const bf16x8*>(b0 + 16 * t * GC_LDA + 32 * sub);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(a0 + 16 * mt * GC_LDA + 32 * sub);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
+    }
+  }
+}
+
+// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
+// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
+template <bool SWIGLU, bool CHECK>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_big(const bf16_t* __restrict__ A,
+                                                                const int32_t* __restrict__ offsets,
+                                                                int e_begin, int e_end,
+                                                                const bf16_t* __restrict__ B1,
+                                                                const bf16_t* __restrict__ B3,
+                                                                int K, int N,
+                                                                bf16_t* __restrict__ C, int ntn) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
+  __shared__ int pre[XG_MAXN + 1];
+  const BigTile bt = schedule_big(offsets, e_begin, e_end, ntn, pre);
+  if (bt.R <= 0) return;
+  const int t = threadIdx.x;
+  const int nb = t & 31;
+  const int64_t estride = (int64_t)K * N;
+  const bf16_t* Bp;
+  int bcol;
+  if (SWIGLU) {
+    Bp = ((nb < 16) ? B1 : B3) + bt.e * estride;
+    bcol = bt.nt * 128 + 8 * (nb & 15);
+  } else {
+    Bp = B1 + bt.e * estride;
+    bcol = bt.nt * 256 + 8 * nb;
+  }
+  const bf16_t* Ablk = A + (int64_t)bt.r0 * K;
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = (K + GC_KS - 1) / GC_KS;
+  BigRegs R;
+  big_load<SWIGLU, CHECK>(R, Ablk, bt.R, K, Bp, N, bcol, 0);
+  big_store<SWIGLU>(R, As[0], Bs[0]);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) big_load<SWIGLU, CHECK>(R, Ablk, bt.R, K, Bp, N, bcol, (st + 1) * GC_KS);
+    big_compute(As[cur], Bs[cur], acc);
+    if (st + 1 < nst) big_store<SWIGLU>(R, As[cur ^ 1], Bs[cur ^ 1]);
+    __syncthreads();
+  }
+  // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile t, rows
+  // 128 wm + 16 mt + 4 g + r of output column base + 8 (i & 7) + t
+  const int lane = t & 63, wave = t >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave & 1, wn = wave >> 1;
+  int ocol;
+  if (SWIGLU) ocol = bt.nt * 128 + 64 * wn + 8 * (i & 7);
+  else ocol = bt.nt * 256 + 128 * wn + 8 * i;
+  const bool store_lane = (SWIGLU ? (i < 8) : true) && ocol < N;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float o[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float a = acc[mt][c][r];
+        if (SWIGLU) {
+          const float b = __shfl_xor(a, 8);
+          o[c] = a / (1.0f + expf(-a)) * b;
+        } else {
+          o[c] = a;
+        }
+      }
+      const int row = 128 * wm + 16 * mt + 4 * g + r;
+      if (store_lane && row < bt.R) {
+        u32x4 pk = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                         pack_bf16x2(o[6], o[7])};
+        *reinterpret_cast<u32x4*>(C + (int64_t)(bt.r0 + row) * N + ocol) = pk;
+      }
+    }
   }
 }
 
@@ -201,21 +466,46 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                               void* y_packed, void*, int e_begin, int e_end, hipStream_t st) {
   if (p.rows_max == 0 || e_end <= e_begin) return hipSuccess;
   if (p.dtype == 1) {
+    // experts with >= XB_TH rows go to the 256 x 256 kernel; no expert can
+    // exceed T rows (top-k picks distinct experts), so small T never needs it
+    const bool big = p.T >= XB_TH;
+    const int th = big ? XB_TH : INT32_MAX;
     const int64_t mblocks = (p.rows_max + XG_BM - 1) / XG_BM + (e_end - e_begin);
+    const int64_t bblocks = (p.rows_max + XB_BM - 1) / XB_BM + (e_end - e_begin);
+    hipError_t e;
+    // GEMM-1 (SwiGLU)
+    if (big) {
+      const int ntn = (p.f + 127) / 128;
+      const bool chk = (p.d % GC_KS) != 0 || (p.f % 128) != 0;
+      auto kb = chk ? grouped_gemm_bf16_big<true, true> : grouped_gemm_bf16_big<true, false>;
+      hipLaunchKernelGGL(kb, dim3((unsigned)(bblocks * ntn)), dim3(256), 0, st,
+                         (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
+                         (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int nb1 = (p.f + 127) / 128;
     const bool chk1 = (p.d % GC_KS) != 0 || (p.f % 128) != 0;
     auto k1 = chk1 ? grouped_gemm_bf16<true, true> : grouped_gemm_bf16<true, false>;
-    hipLaunchKernelGGL(k1, dim3((unsigned)(mblocks * nb1)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k1, dim3((unsigned)(mblocks * nb1)), dim3(64 * XG_NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, nb1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, nb1, th);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // GEMM-2 (down projection)
+    if (big) {
+      const int ntn = (p.d + 255) / 256;
+      const bool chk = (p.f % GC_KS) != 0 || (p.d % 256) != 0;
+      auto kb = chk ? grouped_gemm_bf16_big<false, true> : grouped_gemm_bf16_big<false, false>;
+      hipLaunchKernelGGL(kb, dim3((unsigned)(bblocks * ntn)), dim3(256), 0, st, (const bf16_t*)h,
+                         offsets, e_begin, e_end, (const bf16_t*)w2, (const bf16_t*)nullptr, p.f,
+                         p.d, (bf16_t*)y_packed, ntn);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const int nb2 = (p.d + 255) / 256;
     const bool chk2 = (p.f % GC_KS) != 0 || (p.d % 256) != 0;
     auto k2 = chk2 ? grouped_gemm_bf16<false, true> : grouped_gemm_bf16<false, false>;
-    hipLaunchKernelGGL(k2, dim3((unsigned)(mblocks * nb2)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k2, dim3((unsigned)(mblocks * nb2)), dim3(64 * XG_NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, nb2);
+                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, nb2, th);
     return hipGetLastError();
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);

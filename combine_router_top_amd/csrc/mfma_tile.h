@@ -10,59 +10,88 @@
 //
 // Weights are stored row-major as [K][N] (N contiguous), so a B fragment's 8
 // k-values of one column are N elements apart.  Instead of staging through LDS,
-// each lane loads 8 consecutive rows x 4 consecutive columns (8 bytes per row)
-// and transposes the 8x4 block in registers with byte permutes.  Lane i of
-// group g then owns columns n0 + 4i + c (c = 0..3) for k rows 8g..8g+7, which
-// makes n-tile c the strided column set {n0 + 4i + c : i = 0..15}.  In the
-// output each lane therefore holds 4 consecutive columns of each of its rows,
-// so the epilogue stores 4 elements at once.
+// each lane loads 8 consecutive rows x CPL consecutive columns (2*CPL bytes per
+// row) and transposes the 8 x CPL block in registers with byte permutes.  Lane
+// i of group g then owns columns n0 + CPL*i + c (c = 0..CPL-1) for k rows
+// 8g..8g+7, which makes n-tile c the strided column set {n0 + CPL*i + c}.  In
+// the output each lane therefore holds CPL consecutive columns of each of its
+// rows, so the epilogue stores CPL elements at once.
 #pragma once
 
 #include "common.h"
 
 namespace moe {
 
-struct BRaw {
-  u32x2 row[8];  // row r: columns c0..c3 of k-row 8g + r (bf16 pairs)
+// 8 k-rows x CPL columns of bf16, one register word per row for CPL = 2, two
+// for CPL = 4.
+template <int CPL>
+struct BBlk;
+template <>
+struct BBlk<2> {
+  uint32_t row[8];
+};
+template <>
+struct BBlk<4> {
+  u32x2 row[8];
 };
 
-// Load the 8x4 block at (k-row kb + 8g .. +7, column nc .. nc+3) of a row-major
-// [K][ldb] bf16 matrix; rows >= K or a column group past N read as zeros.
-__device__ __forceinline__ void load_b_block(BRaw& br, const bf16_t* __restrict__ B, int64_t ldb,
-                                             int kb, int K, int nc, int N) {
+template <int CPL>
+__device__ __forceinline__ uint32_t bblk_word(const BBlk<CPL>& b, int r, int w);
+template <>
+__device__ __forceinline__ uint32_t bblk_word<2>(const BBlk<2>& b, int r, int) { return b.row[r]; }
+template <>
+__device__ __forceinline__ uint32_t bblk_word<4>(const BBlk<4>& b, int r, int w) { return b.row[r][w]; }
+
+// Load the block at (k-row kb + 8g .. +7, column nc .. nc+CPL-1) of a
+// row-major [K][ldb] bf16 matrix; rows >= K or a column group past N read as
+// zeros.
+template <int CPL>
+__device__ __forceinline__ void load_b_block(BBlk<CPL>& br, const bf16_t* __restrict__ B,
+                                             int64_t ldb, int kb, int K, int nc, int N) {
   const int g = __lane_id() >> 4;
   const int k0 = kb + 8 * g;
   const bool colok = nc < N;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int k = k0 + r;
-    if (colok && k < K) {
-      br.row[r] = *reinterpret_cast<const u32x2*>(B + (int64_t)k * ldb + nc);
+    if (CPL == 2) {
+      uint32_t v = 0u;
+      if (colok && k < K) v = *reinterpret_cast<const uint32_t*>(B + (int64_t)k * ldb + nc);
+      reinterpret_cast<uint32_t*>(&br)[r] = v;
     } else {
-      br.row[r] = u32x2{0u, 0u};
+      u32x2 v = u32x2{0u, 0u};
+      if (colok && k < K) v = *reinterpret_cast<const u32x2*>(B + (int64_t)k * ldb + nc);
+      reinterpret_cast<u32x2*>(&br)[r] = v;
     }
   }
 }
 
 // Same, without bounds checks (caller guarantees the block is in range).
-__device__ __forceinline__ void load_b_block_nocheck(BRaw& br, const bf16_t* __restrict__ B,
+template <int CPL>
+__device__ __forceinline__ void load_b_block_nocheck(BBlk<CPL>& br, const bf16_t* __restrict__ B,
                                                      int64_t ldb, int kb, int nc) {
   const int g = __lane_id() >> 4;
   const bf16_t* p = B + (int64_t)(kb + 8 * g) * ldb + nc;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) br.row[r] = *reinterpret_cast<const u32x2*>(p + (int64_t)r * ldb);
+  for (int r = 0; r < 8; ++r) {
+    if (CPL == 2)
+      reinterpret_cast<uint32_t*>(&br)[r] = *reinterpret_cast<const uint32_t*>(p + (int64_t)r * ldb);
+    else
+      reinterpret_cast<u32x2*>(&br)[r] = *reinterpret_cast<const u32x2*>(p + (int64_t)r * ldb);
+  }
 }
 
-// Transpose the 8x4 block into 4 B fragments (one per n-tile c).
-__device__ __forceinline__ void transpose_b(const BRaw& br, bf16x8 frag[4]) {
+// Transpose the 8 x CPL block into CPL B fragments (one per n-tile c).
+template <int CPL>
+__device__ __forceinline__ void transpose_b(const BBlk<CPL>& br, bf16x8 (&frag)[CPL]) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < CPL; ++c) {
     const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
     u32x4 t;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = br.row[2 * q][c >> 1];
-      const uint32_t hi = br.row[2 * q + 1][c >> 1];
+      const uint32_t lo = bblk_word<CPL>(br, 2 * q, c >> 1);
+      const uint32_t hi = bblk_word<CPL>(br, 2 * q + 1, c >> 1);
       t[q] = __builtin_amdgcn_perm(hi, lo, sel);
     }
     frag[c] = __builtin_bit_cast(bf16x8, t);

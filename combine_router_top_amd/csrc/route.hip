@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict
                                                         const bf16_t* __restrict__ wg,
                                                         float* __restrict__ part, int T, int d,
                                                         int E, int kchunk) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2 * RW_BM * GC_LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<4, 4, RW_MT>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int m0 = blockIdx.x * RW_BM;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict
   const int col = blockIdx.z * RW_BN + wave * 64 + 4 * i;
   GemmArgs ga{x + (int64_t)m0 * d, d, min(RW_BM, T - m0), wg, E, kbeg, kend, E, col};
   f32x4 acc[RW_MT][4];
-  gemm_mainloop<RW_MT, CHECK>(ga, As, acc);
+  gemm_mainloop<4, 4, RW_MT, CHECK>(ga, As, acc);
   if (col >= E) return;
   float* out = part + (int64_t)split * T * E;
 #pragma unroll

@@ -29,6 +29,10 @@ SMALL = {
     "one_local": W("one_local", 257, 128, 16, 4, 64, 15, 1, "bf16", seed=10),
     "dense_e1": W("dense_e1", 70, 96, 1, 1, 136, 0, 1, "bf16", seed=11),
     "k_equals_e": W("k_equals_e", 90, 64, 6, 6, 48, 1, 4, "bf16", seed=12),
+    # large segments (256 x 256 tile kernel) with row, K and N tails
+    "big_tails": W("big_tails", 1500, 328, 4, 2, 264, 0, 4, "bf16", seed=14),
+    # skewed: some experts on the large-tile kernel, the rest streamed
+    "big_mixed": W("big_mixed", 1200, 256, 16, 4, 256, 0, 8, "bf16", skew=True, seed=15),
 }
 
 _cache = {}
