@@ -18,10 +18,11 @@
 // assignments never travels to the host; the grid is sized for the worst case
 // and surplus workgroups exit after the prologue.
 //
-// GEMM-1 pairs W1 and W3: in each 16-lane group, lanes 0..7 read W1 columns
-// and lanes 8..15 the same W3 columns, so the epilogue combines a lane with
-// lane ^ 8 and writes h directly; the two intermediate products never reach
-// memory.
+// GEMM-1 pairs W1 and W3: the lower half of the waves streams W1 columns and
+// the upper half the same W3 columns (each wave reads one weight matrix, so its
+// buffer descriptor is wave-uniform); after the K loop the upper half passes
+// its products to the lower half through LDS, which applies SiLU(x.W1)*(x.W3)
+// and writes h.  The intermediate products never reach memory.
 //
 // fp32 path (grouped_gemm_f32): one thread per output element, for the small
 // fp32 problems only.
@@ -44,9 +45,9 @@ constexpr int XG_BM = 16 * XG_MTMAX;      // rows per row block
 #endif
 constexpr int XG_NW = MOE_XG_NW;          // waves per workgroup
 constexpr int XG_CPL = MOE_XG_CPL;        // weight columns per lane (2: 4-byte loads, 4: 8-byte)
-constexpr int XG_HW = 128 / XG_NW;        // h columns per wave in GEMM-1 (128 per workgroup)
+constexpr int XG_HW = 256 / XG_NW;        // h columns per wave in GEMM-1 (128 per workgroup, W1 and W3 halves)
 constexpr int XG_OW = 256 / XG_NW;        // output columns per wave in GEMM-2 (256 per workgroup)
-static_assert(XG_HW == 8 * XG_CPL && XG_OW == 16 * XG_CPL, "tile shape");
+static_assert(XG_HW == 16 * XG_CPL && XG_OW == 16 * XG_CPL, "tile shape");
 constexpr int XG_MAXN = 1024;             // max local experts
 
 // Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb.
@@ -105,40 +106,66 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   return rb;
 }
 
-template <bool SWIGLU, int MT, bool CHECK>
+// LDS bf16 elements of the streaming kernel: the A stage buffers, reused after
+// the K loop for the W3 -> W1 accumulator exchange of GEMM-1.
+constexpr int XG_XCH = (XG_NW / 2) * XG_MTMAX * XG_CPL * 4 * 64;  // floats exchanged
+constexpr int XG_LDS = gc_lds_elems<XG_NW, XG_CPL, XG_MTMAX>() > 2 * XG_XCH
+                           ? gc_lds_elems<XG_NW, XG_CPL, XG_MTMAX>() : 2 * XG_XCH;
+
+template <bool SWIGLU, int MT>
 __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bl,
                                           int K, int N, int col, bf16_t* __restrict__ C,
                                           const RowBlock& rb, bf16_t* As) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
   GemmArgs ga{A + (int64_t)rb.r0 * K, K, rb.R, Bl, N, 0, K, N, col};
   f32x4 acc[MT][XG_CPL];
-  gemm_mainloop<XG_NW, XG_CPL, MT, CHECK>(ga, As, acc);
+  gemm_mainloop<XG_NW, XG_CPL, MT>(ga, As, acc);
 
+  // GEMM-1: waves of the upper half hold the x.W3 products of the columns the
+  // lower half holds x.W1 for; they hand them over through LDS.
+  bool store_wave = true;
+  float* xch = reinterpret_cast<float*>(As);
+  if (SWIGLU) {
+    store_wave = wave < XG_NW / 2;
+    const int pair = wave % (XG_NW / 2);
+    float* slot = xch + pair * (XG_MTMAX * XG_CPL * 4 * 64) + lane;
+    if (!store_wave) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < XG_CPL; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) slot[((mt * XG_CPL + c) * 4 + r) * 64] = acc[mt][c][r];
+    }
+    __syncthreads();
+    if (store_wave) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < XG_CPL; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = acc[mt][c][r];
+            const float b = slot[((mt * XG_CPL + c) * 4 + r) * 64];
+            acc[mt][c][r] = a / (1.0f + expf(-a)) * b;
+          }
+    }
+  }
   // epilogue: lane holds XG_CPL consecutive columns (c) of rows 16 mt + 4 g + r
-  const bool store_lane = SWIGLU ? (i < 8) : true;
+  if (!store_wave || col >= N) return;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float o[XG_CPL];
-#pragma unroll
-      for (int c = 0; c < XG_CPL; ++c) {
-        const float a = acc[mt][c][r];
-        if (SWIGLU) {
-          const float b = __shfl_xor(a, 8);  // the W3 product of the same element
-          o[c] = a / (1.0f + expf(-a)) * b;
-        } else {
-          o[c] = a;
-        }
-      }
       const int row = 16 * mt + 4 * g + r;
-      if (store_lane && row < rb.R && col < N) {
+      if (row < rb.R) {
+        bf16_t* dst = C + (int64_t)(rb.r0 + row) * N + col;
         if (XG_CPL == 2) {
-          *reinterpret_cast<uint32_t*>(C + (int64_t)(rb.r0 + row) * N + col) = pack_bf16x2(o[0], o[1]);
+          *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[mt][0][r], acc[mt][1][r]);
         } else {
-          *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * N + col) =
-              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[XG_CPL - 2], o[XG_CPL - 1])};
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc[mt][0][r], acc[mt][1][r]),
+                                                 pack_bf16x2(acc[mt][XG_CPL - 2][r], acc[mt][XG_CPL - 1][r])};
         }
       }
     }
@@ -147,9 +174,8 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
 
 // SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]; 128 columns per WG.
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d];  256 columns per WG.
-// CHECK:  bounds checks on K and N (needed unless K % 64 == 0 and the column
-//         blocks tile N exactly).
-template <bool SWIGLU, bool CHECK>
+// K and N tails are bounded by the buffer descriptors (gemm_core.h).
+template <bool SWIGLU>
 __global__ __launch_bounds__(64 * XG_NW) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
                                                                  const int32_t* __restrict__ offsets,
                                                                  int e_begin, int e_end,
@@ -158,26 +184,32 @@ __global__ __launch_bounds__(64 * XG_NW) void grouped_gemm_bf16(const bf16_t* __
                                                                  int K, int N,
                                                                  bf16_t* __restrict__ C,
                                                                  int nblk_n, int th) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<XG_NW, XG_CPL, XG_MTMAX>()];
+  __shared__ __attribute__((aligned(16))) bf16_t As[XG_LDS];
   __shared__ int pre[XG_MAXN + 1];
-  const RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, th, pre);
+  RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, th, pre);
+  // values from LDS and the wave index are wave-uniform; say so, so that
+  // pointers and buffer descriptors built from them live in scalar registers
+  rb.e = __builtin_amdgcn_readfirstlane(rb.e);
+  rb.r0 = __builtin_amdgcn_readfirstlane(rb.r0);
+  rb.R = __builtin_amdgcn_readfirstlane(rb.R);
+  rb.nb = __builtin_amdgcn_readfirstlane(rb.nb);
   if (rb.R <= 0) return;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = threadIdx.x & 15;
   int col;
   const bf16_t* Bl;
   const int64_t estride = (int64_t)K * N;
-  if (SWIGLU) {  // 16 h columns per wave: lanes 0..7 read W1, lanes 8..15 the same W3 columns
-    col = rb.nb * 128 + wave * XG_HW + XG_CPL * (i & 7);
-    Bl = ((i < 8) ? B1 : B3) + rb.e * estride;
-  } else {       // 32 output columns per wave
+  if (SWIGLU) {  // lower half of the waves streams W1, upper half the same columns of W3
+    col = rb.nb * 128 + (wave % (XG_NW / 2)) * XG_HW + XG_CPL * i;
+    Bl = ((wave < XG_NW / 2) ? B1 : B3) + rb.e * estride;
+  } else {       // output columns per wave
     col = rb.nb * 256 + wave * XG_OW + XG_CPL * i;
     Bl = B1 + rb.e * estride;
   }
   const int mt = (rb.R + 15) >> 4;
   switch (mt) {
 #define XG_CASE(n) \
-  case n: gemm_body<SWIGLU, n, CHECK>(A, Bl, K, N, col, C, rb, As); break;
+  case n: gemm_body<SWIGLU, n>(A, Bl, K, N, col, C, rb, As); break;
     XG_CASE(1) XG_CASE(2) XG_CASE(3) XG_CASE(4) XG_CASE(5)
     XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
 #undef XG_CASE
@@ -484,9 +516,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int nb1 = (p.f + 127) / 128;
-    const bool chk1 = (p.d % GC_KS) != 0 || (p.f % 128) != 0;
-    auto k1 = chk1 ? grouped_gemm_bf16<true, true> : grouped_gemm_bf16<true, false>;
-    hipLaunchKernelGGL(k1, dim3((unsigned)(mblocks * nb1)), dim3(64 * XG_NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3((unsigned)(mblocks * nb1)), dim3(64 * XG_NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
                        (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, nb1, th);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -501,9 +531,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int nb2 = (p.d + 255) / 256;
-    const bool chk2 = (p.f % GC_KS) != 0 || (p.d % 256) != 0;
-    auto k2 = chk2 ? grouped_gemm_bf16<false, true> : grouped_gemm_bf16<false, false>;
-    hipLaunchKernelGGL(k2, dim3((unsigned)(mblocks * nb2)), dim3(64 * XG_NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3((unsigned)(mblocks * nb2)), dim3(64 * XG_NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
                        (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, nb2, th);
     return hipGetLastError();

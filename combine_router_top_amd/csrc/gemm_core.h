@@ -6,19 +6,25 @@
 // 16*CPL weight columns of B (row-major [K][ldb]) straight from memory into
 // registers and transposes them there (mfma_tile.h).
 //
+// All global loads are buffer loads: a per-lane VGPR offset that is fixed for
+// the whole K loop plus a scalar offset that advances per stage.  The loop
+// therefore does no per-lane address arithmetic (such arithmetic needs
+// temporary registers, and when the allocator picks registers that are still
+// the targets of outstanding loads the compiler must wait for those loads,
+// which serialises the pipeline).  The buffer descriptors also bound every
+// access in hardware: reads past the end of a descriptor return zero, which
+// zero-fills the K tail of the weights (rows past kend) and lanes whose
+// columns lie past N (their offset is pushed out of range).  A rows past the
+// block and A columns past kend read finite values from inside the A
+// descriptor; they only meet zero weights or land in accumulator rows that are
+// never stored.
+//
 // Pipeline: K advances in stages of 64.  A ring of 3 register slots holds, per
 // stage, the lane's two 8 x CPL weight blocks and its share of the A tile.
 // While stage s is multiplied, stages s+1 and s+2 are in flight.  Loads retire
 // in order, so A and B of a stage are issued together: when A of stage s+1 is
 // written to LDS at the end of stage s, B of stage s+1 has arrived as well and
 // the two newer stages stay outstanding.  One barrier per stage.
-//
-// Register pressure decides whether this works: if the live ring, the
-// accumulators and the temporaries do not fit, the allocator reuses
-// registers that are still the targets of outstanding loads and the compiler
-// then waits for those loads mid-stage, serialising the pipeline.  The
-// configurations used keep well below the per-wave budget (e.g. 8 waves,
-// 2 columns per lane, 160 rows: 80 accumulator AGPRs).
 #pragma once
 
 #include "common.h"
@@ -29,27 +35,25 @@ namespace moe {
 constexpr int GC_KS = 64;            // K per stage
 constexpr int GC_LDA = GC_KS + 8;    // LDS row stride in bf16 (144 B): fragment reads hit distinct banks
 constexpr int GC_NBUF = 3;           // register ring depth
-#ifndef MOE_GC_STEADY
-#define MOE_GC_STEADY 0              // 1: unguarded three-step loop body (one basic block)
-#endif
+constexpr uint32_t GC_RSRC_W3 = 0x00020000u;  // buffer descriptor word 3 for gfx9-family raw buffers
+constexpr uint32_t GC_OOR = 0x80000000u;      // lane offset that is outside every descriptor
 
 struct GemmArgs {
   const bf16_t* A;   // first row of this block
   int64_t lda;       // A row stride (elements)
-  int R;             // valid rows (1 .. 16*MT); rows >= R are clamped to R-1
-  const bf16_t* B;   // weight matrix [K][ldb]
+  int R;             // rows of this block (>= 1); rows past R are never stored
+  const bf16_t* B;   // weight matrix [K][ldb] (row 0 = k 0)
   int64_t ldb;
   int kbeg, kend;    // K range [kbeg, kend), kbeg a multiple of 8
   int N;             // valid columns of B
   int col;           // this lane's first column (CPL consecutive)
 };
 
-// The A share of a stage always covers whole slabs of 8*NW rows (16*MT
-// rounded up), so every thread has the same number of vectors and no load is
-// predicated.  Rows at or past R are clamped to row R-1: they read valid
-// memory, produce finite values in accumulator rows that are never stored, and
-// keep the loop free of exec-mask branches (branches make the compiler wait for
-// all outstanding loads at their join points).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gc_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)GC_RSRC_W3);
+}
+
 template <int NW, int CPL, int MT>
 struct Pipe {
   static constexpr int NT = 64 * NW;                       // threads
@@ -57,41 +61,52 @@ struct Pipe {
   static constexpr int AROWS = AV * NT / 8;                // rows per LDS stage buffer
   BBlk<CPL> b[GC_NBUF][2];
   u32x4 ar[GC_NBUF][AV];
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[AV];   // per-lane A offsets (bytes), fixed for the loop
+  uint32_t vb;       // per-lane B offset (bytes), fixed for the loop
 };
 
 // LDS bf16 elements needed by gemm_mainloop<NW, CPL, MT>.
 template <int NW, int CPL, int MT>
 constexpr int gc_lds_elems() { return 2 * Pipe<NW, CPL, MT>::AROWS * GC_LDA; }
 
-template <int J, int NW, int CPL, int MT, bool CHECK>
-__device__ __forceinline__ void gc_issue(Pipe<NW, CPL, MT>& P, int st, int nst, const GemmArgs& g) {
-  if (st >= nst) return;
-  const int k0 = g.kbeg + st * GC_KS;
-  if (CHECK) {
-    load_b_block<CPL>(P.b[J][0], g.B, g.ldb, k0, g.kend, g.col, g.N);
-    load_b_block<CPL>(P.b[J][1], g.B, g.ldb, k0 + 32, g.kend, g.col, g.N);
-  } else {
-    load_b_block_nocheck<CPL>(P.b[J][0], g.B, g.ldb, k0, g.col);
-    load_b_block_nocheck<CPL>(P.b[J][1], g.B, g.ldb, k0 + 32, g.col);
-  }
+template <int NW, int CPL, int MT>
+__device__ __forceinline__ void gc_setup(Pipe<NW, CPL, MT>& P, const GemmArgs& g) {
+  // A descriptor spans the block's rows; B descriptor spans rows [0, kend).
+  P.ra = gc_rsrc(g.A, (uint32_t)((int64_t)g.R * g.lda * 2));
+  P.rb = gc_rsrc(g.B, (uint32_t)((int64_t)g.kend * g.ldb * 2));
 #pragma unroll
   for (int q = 0; q < Pipe<NW, CPL, MT>::AV; ++q) {
     const int v = threadIdx.x + Pipe<NW, CPL, MT>::NT * q;
     const int r = min(v >> 3, g.R - 1);
-    const int k = k0 + 8 * (v & 7);
-    if (CHECK) {
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (k < g.kend) val = *reinterpret_cast<const u32x4*>(g.A + (int64_t)r * g.lda + k);
-      P.ar[J][q] = val;
-    } else {
-      P.ar[J][q] = *reinterpret_cast<const u32x4*>(g.A + (int64_t)r * g.lda + k);
-    }
+    P.va[q] = (uint32_t)(((int64_t)r * g.lda + 8 * (v & 7)) * 2);
   }
+  const int grp = (threadIdx.x & 63) >> 4;
+  P.vb = g.col < g.N ? (uint32_t)(((int64_t)(8 * grp) * g.ldb + g.col) * 2) : GC_OOR;
 }
 
 template <int J, int NW, int CPL, int MT>
-__device__ __forceinline__ void gc_stash(Pipe<NW, CPL, MT>& P, int st, int nst, bf16_t* As) {
-  if (st >= nst) return;
+__device__ __forceinline__ void gc_issue(Pipe<NW, CPL, MT>& P, int st, const GemmArgs& g) {
+  const int k0 = g.kbeg + st * GC_KS;
+  const uint32_t row_bytes = (uint32_t)(g.ldb * 2);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t so = (uint32_t)(k0 + 32 * s + r) * row_bytes;
+      if constexpr (CPL == 2)
+        P.b[J][s].row[r] = __builtin_amdgcn_raw_buffer_load_b32(P.rb, P.vb, so, 0);
+      else
+        P.b[J][s].row[r] = __builtin_amdgcn_raw_buffer_load_b64(P.rb, P.vb, so, 0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < Pipe<NW, CPL, MT>::AV; ++q)
+    P.ar[J][q] = __builtin_amdgcn_raw_buffer_load_b128(P.ra, P.va[q], (uint32_t)(k0 * 2), 0);
+}
+
+template <int J, int NW, int CPL, int MT>
+__device__ __forceinline__ void gc_stash(Pipe<NW, CPL, MT>& P, int st, bf16_t* As) {
   bf16_t* dst = As + (st & 1) * (Pipe<NW, CPL, MT>::AROWS * GC_LDA);
 #pragma unroll
   for (int q = 0; q < Pipe<NW, CPL, MT>::AV; ++q) {
@@ -119,25 +134,27 @@ __device__ __forceinline__ void gc_compute(Pipe<NW, CPL, MT>& P, int st, const b
   }
 }
 
-template <int J, int NW, int CPL, int MT, bool CHECK, bool GUARD>
+// Stage st uses ring slot J; it refills slot J-1 (consumed by stage st-1)
+// with stage st+2, multiplies, then writes A of stage st+1 into LDS.  GUARD
+// selects the form with range conditions (prologue/tail); the steady-state
+// form has none, so a whole trip of three steps is one basic block and the
+// loads cannot be sunk towards their use two steps later.  The scheduling
+// barrier after the issue keeps the machine scheduler from doing the same.
+template <int J, bool GUARD, int NW, int CPL, int MT>
 __device__ __forceinline__ void gc_step(Pipe<NW, CPL, MT>& P, int st, int nst, const GemmArgs& g,
                                         bf16_t* As, f32x4 (&acc)[MT][CPL]) {
   if (GUARD && st >= nst) return;
-  if (!GUARD || st + 2 < nst) gc_issue<(J + 2) % GC_NBUF, NW, CPL, MT, CHECK>(P, st + 2, st + 3, g);
-  gc_compute<J, NW, CPL, MT>(P, st, As, acc);
-  if (!GUARD || st + 1 < nst) gc_stash<(J + 1) % GC_NBUF, NW, CPL, MT>(P, st + 1, st + 2, As);
+  if (!GUARD || st + 2 < nst) gc_issue<(J + 2) % GC_NBUF>(P, st + 2, g);
+  __builtin_amdgcn_sched_barrier(0);
+  gc_compute<J>(P, st, As, acc);
+  if (!GUARD || st + 1 < nst) gc_stash<(J + 1) % GC_NBUF>(P, st + 1, As);
   __syncthreads();
 }
 
 // acc[mt][c][r] receives rows 16 mt + 4 (lane / 16) + r, column g.col + c.
 // As must hold gc_lds_elems<NW, CPL, MT>() bf16; g.R >= 1.  All 64*NW threads
 // must call this.
-//
-// The steady-state loop runs three steps per trip with no conditions inside,
-// so all of a trip is one basic block: the loads of stage s+2 cannot be sunk
-// (by the compiler's sinking or scheduling passes) towards their use two
-// steps later.  The last stages run through guarded steps.
-template <int NW, int CPL, int MT, bool CHECK>
+template <int NW, int CPL, int MT>
 __device__ __forceinline__ void gemm_mainloop(const GemmArgs& g, bf16_t* As,
                                               f32x4 (&acc)[MT][CPL]) {
 #pragma unroll
@@ -147,29 +164,22 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& g, bf16_t* As,
   const int nst = (g.kend - g.kbeg + GC_KS - 1) / GC_KS;
   if (nst <= 0) return;
   Pipe<NW, CPL, MT> P;
-  gc_issue<0, NW, CPL, MT, CHECK>(P, 0, nst, g);
-  gc_issue<1, NW, CPL, MT, CHECK>(P, 1, nst, g);
-  gc_stash<0, NW, CPL, MT>(P, 0, nst, As);
+  gc_setup(P, g);
+  gc_issue<0>(P, 0, g);
+  if (nst > 1) gc_issue<1>(P, 1, g);
+  gc_stash<0>(P, 0, As);
   __syncthreads();
   int st = 0;
-#if MOE_GC_STEADY
-  for (; st + 5 <= nst; st += GC_NBUF) {
-    gc_step<0, NW, CPL, MT, CHECK, false>(P, st, nst, g, As, acc);
-    gc_step<1, NW, CPL, MT, CHECK, false>(P, st + 1, nst, g, As, acc);
-    gc_step<2, NW, CPL, MT, CHECK, false>(P, st + 2, nst, g, As, acc);
+  for (; st + 5 <= nst; st += GC_NBUF) {   // stages st .. st+4 exist
+    gc_step<0, false>(P, st, nst, g, As, acc);
+    gc_step<1, false>(P, st + 1, nst, g, As, acc);
+    gc_step<2, false>(P, st + 2, nst, g, As, acc);
   }
-#else
-  for (; st + 5 <= nst; st += GC_NBUF) {
-    gc_step<0, NW, CPL, MT, CHECK, true>(P, st, nst, g, As, acc);
-    gc_step<1, NW, CPL, MT, CHECK, true>(P, st + 1, nst, g, As, acc);
-    gc_step<2, NW, CPL, MT, CHECK, true>(P, st + 2, nst, g, As, acc);
-  }
-#endif
-  // at most 4 stages remain; slot of stage st is st % 3 == 0 here
-  gc_step<0, NW, CPL, MT, CHECK, true>(P, st, nst, g, As, acc);
-  gc_step<1, NW, CPL, MT, CHECK, true>(P, st + 1, nst, g, As, acc);
-  gc_step<2, NW, CPL, MT, CHECK, true>(P, st + 2, nst, g, As, acc);
-  gc_step<0, NW, CPL, MT, CHECK, true>(P, st + 3, nst, g, As, acc);
+  // at most 4 stages remain; the slot of stage st is 0 here
+  gc_step<0, true>(P, st, nst, g, As, acc);
+  gc_step<1, true>(P, st + 1, nst, g, As, acc);
+  gc_step<2, true>(P, st + 2, nst, g, As, acc);
+  gc_step<0, true>(P, st + 3, nst, g, As, acc);
 }
 
 }  // namespace moe

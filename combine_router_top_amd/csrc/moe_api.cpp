@@ -50,6 +50,9 @@ moe_status_t check_problem(const moe_problem_t* p, moe::Prob* out) {
   if (p->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E=%d > 1024 not supported", p->E);
   if (p->d % 8 != 0 || p->f % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "d=%d and f=%d must be multiples of 8", p->d, p->f);
+  const int64_t es = p->dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  if ((int64_t)p->d * p->f * es >= ((int64_t)1 << 31) || (int64_t)p->d * p->E * es >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "a weight matrix exceeds 2 GiB (d=%d f=%d E=%d)", p->d, p->f, p->E);
   const int64_t tk = (int64_t)p->T * p->k;
   if (tk >= (int64_t)1 << 30)
     return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld too large", (long long)tk);

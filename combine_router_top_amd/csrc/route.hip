@@ -31,13 +31,12 @@ constexpr int RW_MT = 4;        // m-tiles per workgroup
 constexpr int RW_BM = 16 * RW_MT;  // tokens per workgroup
 constexpr int RW_BN = 256;      // experts per workgroup (4 waves x 64)
 
-template <bool CHECK>
 __global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict__ x,
                                                         const bf16_t* __restrict__ wg,
                                                         float* __restrict__ part, int T, int d,
                                                         int E, int kchunk) {
   __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<4, 4, RW_MT>()];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, g = lane >> 4;
   const int m0 = blockIdx.x * RW_BM;
   const int split = blockIdx.y;
@@ -46,7 +45,7 @@ __global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict
   const int col = blockIdx.z * RW_BN + wave * 64 + 4 * i;
   GemmArgs ga{x + (int64_t)m0 * d, d, min(RW_BM, T - m0), wg, E, kbeg, kend, E, col};
   f32x4 acc[RW_MT][4];
-  gemm_mainloop<4, 4, RW_MT, CHECK>(ga, As, acc);
+  gemm_mainloop<4, 4, RW_MT>(ga, As, acc);
   if (col >= E) return;
   float* out = part + (int64_t)split * T * E;
 #pragma unroll
@@ -280,10 +279,8 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
   const int S = route_splits(p);
   if (kind == ROUTE_WIDE) {
     const int kchunk = route_kchunk(p, S);
-    const bool check = (p.E % RW_BN) != 0 || (p.d % GC_KS) != 0;
     dim3 grid((p.T + RW_BM - 1) / RW_BM, S, (p.E + RW_BN - 1) / RW_BN);
-    auto kern = check ? router_wide_mfma<true> : router_wide_mfma<false>;
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wg, part, p.T,
+    hipLaunchKernelGGL(router_wide_mfma, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wg, part, p.T,
                        p.d, p.E, kchunk);
   } else if (kind == ROUTE_NARROW) {
     dim3 grid((p.T + RN_ROWS - 1) / RN_ROWS);
