@@ -221,18 +221,25 @@ __global__ __launch_bounds__(64 * XG_NW) void grouped_gemm_bf16(const bf16_t* __
 // large segments: 256 x 256 tiles, both operands through LDS
 // ---------------------------------------------------------------------------
 // For experts with at least XB_TH rows the weight-streaming kernel above would
-// re-read the weights once per 160-row block; here a workgroup computes a
-// 256-row x 256-weight-column tile with 4 waves of 128 x 128 (accumulators in
-// AGPRs).  Per 64-K stage every thread loads 8 A vectors and one 8 x 8 weight
-// block into registers (the next stage is in flight while the current one is
-// multiplied), transposes the weight block and writes both into the other LDS
-// buffer.  Weight columns are placed in LDS so that each lane's 8 n-tiles are
-// 8 consecutive output columns (16-byte stores), and for GEMM-1 so that W1 and
-// W3 of one column meet in lanes i and i ^ 8.
+// re-read the weights once per 160-row block; here a workgroup of 8 waves
+// computes a 256-row x 256-weight-column tile, each wave 128 x 64
+// (accumulators in AGPRs, two waves per SIMD).  Per 64-K stage every thread
+// loads 4 A vectors and one 8 x 4 weight block with buffer loads (fixed lane
+// offsets, scalar stage offsets); the next stage is in flight while the
+// current one is multiplied; the weight block is transposed in registers and
+// both are written into the other LDS buffer.  Weight columns are placed in
+// LDS so that each lane's 4 n-tiles are 4 consecutive output columns (8-byte
+// stores), and for GEMM-1 so that W1 and W3 of one column meet in lanes i and
+// i ^ 8.  The lower four waves load W1 blocks, the upper four W3 blocks, so
+// every buffer descriptor is wave-uniform.
 constexpr int XB_BM = 256;
 constexpr int XB_BN = 256;      // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
+constexpr int XB_NW = 8;        // waves per workgroup
 constexpr int XB_TH = 320;      // row count from which an expert uses this kernel
-constexpr int XB_GM = 4;        // m-tiles grouped together along the XCD-local order
+#ifndef MOE_XB_GM
+#define MOE_XB_GM 8
+#endif
+constexpr int XB_GM = MOE_XB_GM; // m-tiles grouped together along the XCD-local order
 
 struct BigTile {
   int e, r0, R, nt;
@@ -288,176 +295,179 @@ __device__ BigTile schedule_big(const int32_t* __restrict__ offsets, int e_begin
 }
 
 struct BigRegs {
-  u32x4 a[8];
-  u32x4 b[8];
+  u32x4 a[4];
+  u32x2 b[8];
 };
 
-template <bool SWIGLU, bool CHECK>
-__device__ __forceinline__ void big_load(BigRegs& R, const bf16_t* __restrict__ Ablk, int Rrows,
-                                         int K, const bf16_t* __restrict__ Bp, int N, int bcol,
-                                         int k0) {
-  // Rows past Rrows are clamped to the last valid row (finite values in rows
-  // that are never stored), so the unchecked path has no predicated loads.
-  const int t = threadIdx.x;
-  const int k = k0 + 8 * (t & 7);
+// Per-thread fixed state of the large-tile loop: buffer descriptors (wave
+// uniform) and byte offsets that do not change with K.
+struct BigCtx {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[4];   // A rows (t >> 3) + 64 j, 16-byte chunk t & 7
+  uint32_t vb;      // B block: k rows 8 kb .. 8 kb + 7 (via scalar offsets), 4 columns
+  uint32_t ldb2;    // B row bytes
+  int kb, nb;       // block coordinates inside the 64 x 256 weight stage (nb: 4-column group)
+};
+
+__device__ __forceinline__ void big_issue(BigRegs& R, const BigCtx& c, int k0) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = min((t >> 3) + 32 * j, Rrows - 1);
-    if (CHECK) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (k < K) v = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
-      R.a[j] = v;
-    } else {
-      R.a[j] = *reinterpret_cast<const u32x4*>(Ablk + (int64_t)r * K + k);
-    }
-  }
-  const int kb = t >> 5;
+  for (int j = 0; j < 4; ++j)
+    R.a[j] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.va[j], (uint32_t)(k0 * 2), 0);
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int kk = k0 + 8 * kb + r;
-    if (CHECK) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (kk < K && bcol < N) v = *reinterpret_cast<const u32x4*>(Bp + (int64_t)kk * N + bcol);
-      R.b[r] = v;
-    } else {
-      R.b[r] = *reinterpret_cast<const u32x4*>(Bp + (int64_t)kk * N + bcol);
-    }
-  }
+  for (int r = 0; r < 8; ++r)
+    R.b[r] = __builtin_amdgcn_raw_buffer_load_b64(c.rb, c.vb, (uint32_t)(k0 + r) * c.ldb2, 0);
 }
 
-// LDS row (within the 256-row B^T tile) of weight column c of this thread's block.
+// LDS row (within the 256-row B^T tile) of weight column c (0..3) of 4-column
+// group nb.  GEMM-1: nb 0..31 are W1 columns 4 nb .., nb 32..63 the same W3
+// columns; wave slab wn holds h columns 32 wn .. 32 wn + 31, lane i (< 8) of
+// n-tile t the h column 32 wn + 4 i + t, lane i + 8 its W3 twin.  GEMM-2: wave
+// slab wn holds weight columns 64 wn .. 64 wn + 63, lane i of n-tile t column
+// 64 wn + 4 i + t.
 template <bool SWIGLU>
 __device__ __forceinline__ int big_brow(int nb, int c) {
   if (SWIGLU) {
-    const int m3 = nb >> 4;             // 0: W1, 1: W3
-    const int hc = 8 * (nb & 15) + c;   // h column within the tile (0..127)
-    const int wn = hc >> 6, hw = hc & 63;
-    return 128 * wn + 16 * (hw & 7) + 8 * m3 + (hw >> 3);
+    const int m3 = nb >> 5;
+    const int hc = 4 * (nb & 31) + c;   // 0..127
+    const int wn = hc >> 5, hw = hc & 31;
+    return 64 * wn + 16 * (hw & 3) + 8 * m3 + (hw >> 2);
   } else {
-    const int wc = 8 * nb + c;          // weight column within the tile (0..255)
-    const int wn = wc >> 7, cw = wc & 127;
-    return 128 * wn + 16 * (cw & 7) + (cw >> 3);
+    const int wc = 4 * nb + c;          // 0..255
+    const int wn = wc >> 6, cw = wc & 63;
+    return 64 * wn + 16 * (cw & 3) + (cw >> 2);
   }
 }
 
 template <bool SWIGLU>
-__device__ __forceinline__ void big_store(const BigRegs& R, bf16_t* As, bf16_t* Bs) {
+__device__ __forceinline__ void big_store(const BigRegs& R, const BigCtx& c, bf16_t* As, bf16_t* Bs) {
   const int t = threadIdx.x;
-  const int s = t & 7;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (t >> 3) + 32 * j;
-    *reinterpret_cast<u32x4*>(As + r * GC_LDA + 8 * s) = R.a[j];
-  }
-  const int kb = t >> 5, nb = t & 31;
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<u32x4*>(As + ((t >> 3) + 64 * j) * GC_LDA + 8 * (t & 7)) = R.a[j];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+  for (int col = 0; col < 4; ++col) {
+    const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
     u32x4 v;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      v[q] = __builtin_amdgcn_perm(R.b[2 * q + 1][c >> 1], R.b[2 * q][c >> 1], sel);
-    *reinterpret_cast<u32x4*>(Bs + big_brow<SWIGLU>(nb, c) * GC_LDA + 8 * kb) = v;
+      v[q] = __builtin_amdgcn_perm(R.b[2 * q + 1][col >> 1], R.b[2 * q][col >> 1], sel);
+    *reinterpret_cast<u32x4*>(Bs + big_brow<SWIGLU>(c.nb, col) * GC_LDA + 8 * c.kb) = v;
   }
 }
 
-__device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs,
-                                            f32x4 (&acc)[8][8]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs, int wm, int wn,
+                                            f32x4 (&acc)[8][4]) {
+  const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
   const bf16_t* a0 = As + (128 * wm + i) * GC_LDA + 8 * g;
-  const bf16_t* b0 = Bs + (128 * wn + i) * GC_LDA + 8 * g;
+  const bf16_t* b0 = Bs + (64 * wn + i) * GC_LDA + 8 * g;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
-    bf16x8 bf[8];
+    bf16x8 bf[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 4; ++t)
       bf[t] = *reinterpret_cast<const bf16x8*>(b0 + 16 * t * GC_LDA + 32 * sub);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(a0 + 16 * mt * GC_LDA + 32 * sub);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
     }
   }
 }
 
 // SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
-template <bool SWIGLU, bool CHECK>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_big(const bf16_t* __restrict__ A,
-                                                                const int32_t* __restrict__ offsets,
-                                                                int e_begin, int e_end,
-                                                                const bf16_t* __restrict__ B1,
-                                                                const bf16_t* __restrict__ B3,
-                                                                int K, int N,
-                                                                bf16_t* __restrict__ C, int ntn) {
+// K and N tails are bounded by the buffer descriptors.
+template <bool SWIGLU>
+__global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int e_begin, int e_end,
+    const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3, int K, int N,
+    bf16_t* __restrict__ C, int ntn) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
   __shared__ int pre[XG_MAXN + 1];
-  const BigTile bt = schedule_big(offsets, e_begin, e_end, ntn, pre);
+  BigTile bt = schedule_big(offsets, e_begin, e_end, ntn, pre);
+  bt.e = __builtin_amdgcn_readfirstlane(bt.e);
+  bt.r0 = __builtin_amdgcn_readfirstlane(bt.r0);
+  bt.R = __builtin_amdgcn_readfirstlane(bt.R);
+  bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
   if (bt.R <= 0) return;
   const int t = threadIdx.x;
-  const int nb = t & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t estride = (int64_t)K * N;
+  BigCtx c;
   const bf16_t* Bp;
   int bcol;
-  if (SWIGLU) {
-    Bp = ((nb < 16) ? B1 : B3) + bt.e * estride;
-    bcol = bt.nt * 128 + 8 * (nb & 15);
+  if (SWIGLU) {  // waves 0-3 load W1 blocks, waves 4-7 the same W3 blocks
+    const int u = t & 255;
+    c.kb = u >> 5;
+    c.nb = (u & 31) + (wave >= 4 ? 32 : 0);
+    Bp = (wave < 4 ? B1 : B3) + bt.e * estride;
+    bcol = bt.nt * 128 + 4 * (u & 31);
   } else {
+    c.kb = t >> 6;
+    c.nb = t & 63;
     Bp = B1 + bt.e * estride;
-    bcol = bt.nt * 256 + 8 * nb;
+    bcol = bt.nt * 256 + 4 * c.nb;
   }
   const bf16_t* Ablk = A + (int64_t)bt.r0 * K;
-  f32x4 acc[8][8];
+  c.ra = gc_rsrc(Ablk, (uint32_t)((int64_t)bt.R * K * 2));
+  c.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = min((t >> 3) + 64 * j, bt.R - 1);
+    c.va[j] = (uint32_t)(((int64_t)r * K + 8 * (t & 7)) * 2);
+  }
+  c.vb = bcol < N ? (uint32_t)(((int64_t)(8 * c.kb) * N + bcol) * 2) : GC_OOR;
+  c.ldb2 = (uint32_t)(N * 2);
+
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4 acc[8][4];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 4; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nst = (K + GC_KS - 1) / GC_KS;
   BigRegs R;
-  big_load<SWIGLU, CHECK>(R, Ablk, bt.R, K, Bp, N, bcol, 0);
-  big_store<SWIGLU>(R, As[0], Bs[0]);
+  big_issue(R, c, 0);
+  big_store<SWIGLU>(R, c, As[0], Bs[0]);
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
     const int cur = st & 1;
-    if (st + 1 < nst) big_load<SWIGLU, CHECK>(R, Ablk, bt.R, K, Bp, N, bcol, (st + 1) * GC_KS);
-    big_compute(As[cur], Bs[cur], acc);
-    if (st + 1 < nst) big_store<SWIGLU>(R, As[cur ^ 1], Bs[cur ^ 1]);
+    if (st + 1 < nst) big_issue(R, c, (st + 1) * GC_KS);
+    __builtin_amdgcn_sched_barrier(0);
+    big_compute(As[cur], Bs[cur], wm, wn, acc);
+    if (st + 1 < nst) big_store<SWIGLU>(R, c, As[cur ^ 1], Bs[cur ^ 1]);
     __syncthreads();
   }
-  // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile t, rows
-  // 128 wm + 16 mt + 4 g + r of output column base + 8 (i & 7) + t
-  const int lane = t & 63, wave = t >> 6;
+  // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile q, rows
+  // 128 wm + 16 mt + 4 g + r of output column base + 4 (i or i & 7) + q
+  const int lane = t & 63;
   const int i = lane & 15, g = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
   int ocol;
-  if (SWIGLU) ocol = bt.nt * 128 + 64 * wn + 8 * (i & 7);
-  else ocol = bt.nt * 256 + 128 * wn + 8 * i;
+  if (SWIGLU) ocol = bt.nt * 128 + 32 * wn + 4 * (i & 7);
+  else ocol = bt.nt * 256 + 64 * wn + 4 * i;
   const bool store_lane = (SWIGLU ? (i < 8) : true) && ocol < N;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float o[8];
+      float o[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float a = acc[mt][c][r];
+      for (int q = 0; q < 4; ++q) {
+        const float a = acc[mt][q][r];
         if (SWIGLU) {
           const float b = __shfl_xor(a, 8);
-          o[c] = a / (1.0f + expf(-a)) * b;
+          o[q] = a / (1.0f + expf(-a)) * b;
         } else {
-          o[c] = a;
+          o[q] = a;
         }
       }
       const int row = 128 * wm + 16 * mt + 4 * g + r;
-      if (store_lane && row < bt.R) {
-        u32x4 pk = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                         pack_bf16x2(o[6], o[7])};
-        *reinterpret_cast<u32x4*>(C + (int64_t)(bt.r0 + row) * N + ocol) = pk;
-      }
+      if (store_lane && row < bt.R)
+        *reinterpret_cast<u32x2*>(C + (int64_t)(bt.r0 + row) * N + ocol) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
   }
 }
@@ -508,9 +518,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // GEMM-1 (SwiGLU)
     if (big) {
       const int ntn = (p.f + 127) / 128;
-      const bool chk = (p.d % GC_KS) != 0 || (p.f % 128) != 0;
-      auto kb = chk ? grouped_gemm_bf16_big<true, true> : grouped_gemm_bf16_big<true, false>;
-      hipLaunchKernelGGL(kb, dim3((unsigned)(bblocks * ntn)), dim3(256), 0, st,
+      hipLaunchKernelGGL(grouped_gemm_bf16_big<true>, dim3((unsigned)(bblocks * ntn)), dim3(64 * XB_NW), 0, st,
                          (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
                          (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -523,9 +531,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // GEMM-2 (down projection)
     if (big) {
       const int ntn = (p.d + 255) / 256;
-      const bool chk = (p.f % GC_KS) != 0 || (p.d % 256) != 0;
-      auto kb = chk ? grouped_gemm_bf16_big<false, true> : grouped_gemm_bf16_big<false, false>;
-      hipLaunchKernelGGL(kb, dim3((unsigned)(bblocks * ntn)), dim3(256), 0, st, (const bf16_t*)h,
+      hipLaunchKernelGGL(grouped_gemm_bf16_big<false>, dim3((unsigned)(bblocks * ntn)), dim3(64 * XB_NW), 0, st, (const bf16_t*)h,
                          offsets, e_begin, e_end, (const bf16_t*)w2, (const bf16_t*)nullptr, p.f,
                          p.d, (bf16_t*)y_packed, ntn);
       if ((e = hipGetLastError()) != hipSuccess) return e;
