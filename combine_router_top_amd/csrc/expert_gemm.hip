@@ -7,11 +7,11 @@
 //   GEMM-2:  y_packed[R] = rnd(h[R] W2_e)
 //
 // bf16 path (grouped_gemm_bf16).  A workgroup owns one row block of one
-// expert (up to 160 rows) and one column block; every weight byte of that
+// expert (up to 160 or 80 rows, see XGCfg) and one column block; every weight byte of that
 // column block is streamed from HBM exactly once per row block, which is the
 // bound for the segment sizes of a sparse MoE layer (about 4..160 rows per
 // expert).  8 waves (2 per SIMD) share the A rows through LDS; each wave
-// streams its own weight columns (2 per lane) straight from HBM into
+// streams its own weight columns (2 or 4 per lane) straight from HBM into
 // registers and transposes them there into MFMA B fragments (mfma_tile.h,
 // gemm_core.h).  The row-block schedule is derived on the
 // device from `offsets` in the workgroup prologue, so the number of local
@@ -28,131 +28,183 @@
 // fp32 problems only.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "gemm_core.h"
 
 namespace moe {
 
-constexpr int XG_MTMAX = 10;              // m-tiles per row block
-constexpr int XG_BM = 16 * XG_MTMAX;      // rows per row block
-// Build-time tile shape (a tuning choice, not a behaviour switch).
-#ifndef MOE_XG_NW
-#define MOE_XG_NW 8
-#endif
-#ifndef MOE_XG_CPL
-#define MOE_XG_CPL 2
-#endif
-constexpr int XG_NW = MOE_XG_NW;          // waves per workgroup
-constexpr int XG_CPL = MOE_XG_CPL;        // weight columns per lane (2: 4-byte loads, 4: 8-byte)
-constexpr int XG_HW = 256 / XG_NW;        // h columns per wave in GEMM-1 (128 per workgroup, W1 and W3 halves)
-constexpr int XG_OW = 256 / XG_NW;        // output columns per wave in GEMM-2 (256 per workgroup)
-static_assert(XG_HW == 16 * XG_CPL && XG_OW == 16 * XG_CPL, "tile shape");
 constexpr int XG_MAXN = 1024;             // max local experts
 
-// Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb.
+// Tile configurations of the streaming kernel.  "Wide" suits segments of
+// ~100-160 rows (prefill): 160-row blocks, 2 weight columns per lane; "thin"
+// suits segments of a few rows (decode), where the kernel is a pure weight
+// stream and wider (8-byte) weight loads keep the load-instruction rate
+// down: 80-row blocks, 4 columns per lane.  The host picks one from the
+// expected rows per expert.
+template <int NW_, int CPL_, int MTMAX_, int NB_>
+struct XGCfg {
+  static constexpr int NB = NB_;                 // register ring depth
+  static constexpr int NW = NW_;                 // waves per workgroup
+  static constexpr int CPL = CPL_;               // weight columns per lane
+  static constexpr int MTMAX = MTMAX_;           // m-tiles per row block
+  static constexpr int BM = 16 * MTMAX;          // rows per row block
+  static constexpr int HW = 16 * CPL;            // h columns per wave in GEMM-1
+  static constexpr int WG_H = (NW / 2) * HW;     // h columns per workgroup (W1 and W3 halves)
+  static constexpr int OW = 16 * CPL;            // output columns per wave in GEMM-2
+  static constexpr int WG_O = NW * OW;           // output columns per workgroup
+  static constexpr int COLS = WG_O;              // weight columns per workgroup (both GEMMs)
+  // LDS: the A stage buffers, reused after the K loop for the W3 -> W1
+  // accumulator exchange of GEMM-1.
+  static constexpr int XCH = (NW / 2) * MTMAX * CPL * 4 * 64;  // floats exchanged
+  static constexpr int LDS = gc_lds_elems<NW, CPL, MTMAX>() > 2 * XCH
+                                 ? gc_lds_elems<NW, CPL, MTMAX>() : 2 * XCH;
+};
+using XGWide = XGCfg<8, 2, 10, 3>;
+using XGThin = XGCfg<8, 4, 5, 2>;
+
+// Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb,
+// tile class (0: thin, 1: wide).
 struct RowBlock {
-  int e, r0, R, nb;
+  int e, r0, R, nb, cls;
 };
 
-// Schedule from `offsets` (computed by every workgroup, a few hundred cycles):
-// expert e in [e_begin, e_end) has ceil(count_e / XG_BM) row blocks, each with
-// nblk_n column blocks.  The G = (total row blocks) * nblk_n live workgroups
-// are renumbered so that every XCD (workgroup id mod 8 on this part) receives
-// a contiguous range of (row block, column block) pairs: all column blocks of
-// one row block then share one L2 for their A rows.  R = 0 means "exit".
+// Segments of at most XG_THIN_MAX rows stream through the thin tiles, larger
+// ones (below the large-tile threshold) through the wide tiles.
+#ifndef MOE_XG_THIN_MAX
+#define MOE_XG_THIN_MAX 48
+#endif
+constexpr int XG_THIN_MAX = MOE_XG_THIN_MAX;
+
+static_assert(XG_THIN_MAX <= XGThin::BM, "a thin segment is one row block");
+// Work of a block in units of a wide block: the path is bound by the weight
+// stream, which grows with the block's column count.
+constexpr int XG_WT_THIN = XGThin::COLS / XGWide::COLS;
+static_assert(XG_WT_THIN * XGWide::COLS == XGThin::COLS, "thin columns a multiple of wide ones");
+
+// Blocks of class `cls` of one expert with `cnt` rows (0 for the other class).
+__device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls) {
+  if (cnt <= 0 || cnt >= th || (cnt <= XG_THIN_MAX ? 0 : 1) != cls) return 0;
+  if (cls == 0) return (ncols + XGThin::COLS - 1) / XGThin::COLS;
+  return (cnt + XGWide::BM - 1) / XGWide::BM * ((ncols + XGWide::COLS - 1) / XGWide::COLS);
+}
+
+// Schedule from `offsets` (computed by every workgroup, a few hundred cycles).
+// Experts in [e_begin, e_end) with fewer than `th` rows contribute (row block,
+// column block) pairs of their tile class.  The blocks are listed thin class
+// first, then wide, each by ascending expert; a thin block weighs XG_WT_THIN,
+// a wide one 1, and block i starts at the running sum of the weights before
+// it.  XCD x (workgroup id mod 8 on this part) takes the blocks that start in
+// [ceil(x W / 8), ceil((x + 1) W / 8)) of the total work W, the q-th of them
+// going to its q-th workgroup.  Every XCD thus gets an equal share of the
+// weight stream, the column blocks of one row block mostly share one L2 for
+// their A rows, and within an XCD the longer thin blocks start first.  The
+// grid needs 8 ceil(W / 8) workgroups at most.  R = 0 means "exit".
+// `pre` holds 2 (XG_MAXN + 1) ints.
 __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, int e_end,
-                             int nblk_n, int th, int* pre) {
+                             int th, int ncols, int* pre) {
   const int ne = e_end - e_begin;
+  int* prew = pre + XG_MAXN + 1;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int carry = 0;
+    int ct = 0, cw = 0;
     for (int j0 = 0; j0 < ne; j0 += 64) {
       const int j = j0 + lane;
       const int cnt = j < ne ? offsets[e_begin + j + 1] - offsets[e_begin + j] : 0;
-      const int nb = cnt < th ? (cnt + XG_BM - 1) / XG_BM : 0;
-      int x = nb;
+      int xt = xg_blocks(cnt, th, ncols, 0);
+      int xw = xg_blocks(cnt, th, ncols, 1);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
+        const int yt = __shfl_up(xt, off);
+        const int yw = __shfl_up(xw, off);
+        if (lane >= off) { xt += yt; xw += yw; }
       }
-      if (j < ne) pre[j] = carry + x;
-      carry += __shfl(x, 63);
+      if (j < ne) { pre[j] = ct + xt; prew[j] = cw + xw; }
+      ct += __shfl(xt, 63);
+      cw += __shfl(xw, 63);
     }
-    if (lane == 0) pre[XG_MAXN] = carry;
+    if (lane == 0) { pre[XG_MAXN] = ct; prew[XG_MAXN] = cw; }
   }
   __syncthreads();
-  RowBlock rb{0, 0, 0, 0};
-  const int G = pre[XG_MAXN] * nblk_n;
-  const int b = blockIdx.x;
-  if (b >= G) return rb;
-  const int xcd = b & 7, q = b >> 3;
-  const int L = xcd * (G >> 3) + min(xcd, G & 7) + q;
-  const int mb = L / nblk_n;
-  rb.nb = L - mb * nblk_n;
-  int lo = 0, hi = ne - 1;  // first j with pre[j] > mb
+  RowBlock rb{0, 0, 0, 0, 0};
+  const int nth = pre[XG_MAXN], nwd = prew[XG_MAXN];
+  const int wth = XG_WT_THIN * nth;                  // work of the thin blocks
+  const int W = wth + nwd;
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int w0 = (xcd * W + 7) >> 3, w1 = ((xcd + 1) * W + 7) >> 3;
+  // first block starting at or after w0, then this workgroup's block
+  const int i0 = w0 <= wth ? (w0 + XG_WT_THIN - 1) / XG_WT_THIN : nth + (w0 - wth);
+  const int i = i0 + q;
+  if (i >= nth + nwd) return rb;
+  const int start = i < nth ? XG_WT_THIN * i : wth + (i - nth);
+  if (start >= w1) return rb;
+  rb.cls = i < nth ? 0 : 1;
+  const int* P = rb.cls ? prew : pre;
+  const int L = rb.cls ? i - nth : i;
+  int lo = 0, hi = ne - 1;  // first j with P[j] > L
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (pre[mid] > mb) hi = mid; else lo = mid + 1;
+    if (P[mid] > L) hi = mid; else lo = mid + 1;
   }
   const int e = e_begin + lo;
-  const int jb = mb - (lo ? pre[lo - 1] : 0);
+  const int local = L - (lo ? P[lo - 1] : 0);
   const int o = offsets[e];
   const int cnt = offsets[e + 1] - o;
+  const int bm = rb.cls ? XGWide::BM : XGThin::BM;
+  const int cols = rb.cls ? XGWide::COLS : XGThin::COLS;
+  const int nblk = (ncols + cols - 1) / cols;
+  const int jb = local / nblk;
+  rb.nb = local - jb * nblk;
   rb.e = e;
-  rb.r0 = o + jb * XG_BM;
-  rb.R = min(XG_BM, cnt - jb * XG_BM);
+  rb.r0 = o + jb * bm;
+  rb.R = min(bm, cnt - jb * bm);
   return rb;
 }
 
-// LDS bf16 elements of the streaming kernel: the A stage buffers, reused after
-// the K loop for the W3 -> W1 accumulator exchange of GEMM-1.
-constexpr int XG_XCH = (XG_NW / 2) * XG_MTMAX * XG_CPL * 4 * 64;  // floats exchanged
-constexpr int XG_LDS = gc_lds_elems<XG_NW, XG_CPL, XG_MTMAX>() > 2 * XG_XCH
-                           ? gc_lds_elems<XG_NW, XG_CPL, XG_MTMAX>() : 2 * XG_XCH;
-
-template <bool SWIGLU, int MT>
+template <class Cfg, bool SWIGLU, int MT>
 __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bl,
                                           int K, int N, int col, bf16_t* __restrict__ C,
                                           const RowBlock& rb, bf16_t* As) {
+  constexpr int CPL = Cfg::CPL, NW = Cfg::NW;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   GemmArgs ga{A + (int64_t)rb.r0 * K, K, rb.R, Bl, N, 0, K, N, col};
-  f32x4 acc[MT][XG_CPL];
-  gemm_mainloop<XG_NW, XG_CPL, MT>(ga, As, acc);
+  f32x4 acc[MT][CPL];
+  gemm_mainloop<NW, CPL, MT, Cfg::NB>(ga, As, acc);
 
   // GEMM-1: waves of the upper half hold the x.W3 products of the columns the
   // lower half holds x.W1 for; they hand them over through LDS.
   bool store_wave = true;
   float* xch = reinterpret_cast<float*>(As);
   if (SWIGLU) {
-    store_wave = wave < XG_NW / 2;
-    const int pair = wave % (XG_NW / 2);
-    float* slot = xch + pair * (XG_MTMAX * XG_CPL * 4 * 64) + lane;
+    store_wave = wave < NW / 2;
+    const int pair = wave % (NW / 2);
+    float* slot = xch + pair * (Cfg::MTMAX * CPL * 4 * 64) + lane;
     if (!store_wave) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int c = 0; c < XG_CPL; ++c)
+        for (int c = 0; c < CPL; ++c)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) slot[((mt * XG_CPL + c) * 4 + r) * 64] = acc[mt][c][r];
+          for (int r = 0; r < 4; ++r) slot[((mt * CPL + c) * 4 + r) * 64] = acc[mt][c][r];
     }
     __syncthreads();
     if (store_wave) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int c = 0; c < XG_CPL; ++c)
+        for (int c = 0; c < CPL; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float a = acc[mt][c][r];
-            const float b = slot[((mt * XG_CPL + c) * 4 + r) * 64];
+            const float b = slot[((mt * CPL + c) * 4 + r) * 64];
             acc[mt][c][r] = a / (1.0f + expf(-a)) * b;
           }
     }
   }
-  // epilogue: lane holds XG_CPL consecutive columns (c) of rows 16 mt + 4 g + r
+  // epilogue: lane holds CPL consecutive columns (c) of rows 16 mt + 4 g + r
   if (!store_wave || col >= N) return;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -161,60 +213,80 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
       const int row = 16 * mt + 4 * g + r;
       if (row < rb.R) {
         bf16_t* dst = C + (int64_t)(rb.r0 + row) * N + col;
-        if (XG_CPL == 2) {
+        if constexpr (CPL == 2) {
           *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[mt][0][r], acc[mt][1][r]);
         } else {
           *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(acc[mt][0][r], acc[mt][1][r]),
-                                                 pack_bf16x2(acc[mt][XG_CPL - 2][r], acc[mt][XG_CPL - 1][r])};
+                                                 pack_bf16x2(acc[mt][2][r], acc[mt][3][r])};
         }
       }
     }
   }
 }
 
-// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]; 128 columns per WG.
-// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d];  256 columns per WG.
+// One streamed row block of class Cfg.
+template <class Cfg, bool SWIGLU>
+__device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
+                                             const bf16_t* __restrict__ B3, int K, int N,
+                                             bf16_t* __restrict__ C, const RowBlock& rb, int wave,
+                                             bf16_t* As) {
+  const int i = threadIdx.x & 15;
+  int col;
+  const bf16_t* Bl;
+  const int64_t estride = (int64_t)K * N;
+  if (SWIGLU) {  // lower half of the waves streams W1, upper half the same columns of W3
+    col = rb.nb * Cfg::WG_H + (wave % (Cfg::NW / 2)) * Cfg::HW + Cfg::CPL * i;
+    Bl = ((wave < Cfg::NW / 2) ? B1 : B3) + rb.e * estride;
+  } else {       // output columns per wave
+    col = rb.nb * Cfg::WG_O + wave * Cfg::OW + Cfg::CPL * i;
+    Bl = B1 + rb.e * estride;
+  }
+  const int mt = (rb.R + 15) >> 4;
+  switch (mt) {
+#define XG_CASE(n) \
+  case n: if constexpr (n <= Cfg::MTMAX) gemm_body<Cfg, SWIGLU, n>(A, Bl, K, N, col, C, rb, As); break;
+    XG_CASE(1) XG_CASE(2) XG_CASE(3) XG_CASE(4) XG_CASE(5)
+    XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
+#undef XG_CASE
+    default: break;
+  }
+}
+
+static_assert(XGThin::NW == XGWide::NW, "one workgroup size for both tile classes");
+static_assert(XGThin::WG_H * 2 == XGThin::COLS && XGWide::WG_H * 2 == XGWide::COLS,
+              "per workgroup: GEMM-1 streams WG_H columns of W1 and of W3, GEMM-2 COLS columns");
+constexpr int XG_LDS = XGThin::LDS > XGWide::LDS ? XGThin::LDS : XGWide::LDS;
+
+// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
+// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
+// Segments with fewer than `th` rows; each picks its tile class by row count.
 // K and N tails are bounded by the buffer descriptors (gemm_core.h).
 template <bool SWIGLU>
-__global__ __launch_bounds__(64 * XG_NW) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
-                                                                 const int32_t* __restrict__ offsets,
-                                                                 int e_begin, int e_end,
-                                                                 const bf16_t* __restrict__ B1,
-                                                                 const bf16_t* __restrict__ B3,
-                                                                 int K, int N,
-                                                                 bf16_t* __restrict__ C,
-                                                                 int nblk_n, int th) {
+__global__ __launch_bounds__(64 * XGWide::NW) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
+                                                                     const int32_t* __restrict__ offsets,
+                                                                     int e_begin, int e_end,
+                                                                     const bf16_t* __restrict__ B1,
+                                                                     const bf16_t* __restrict__ B3,
+                                                                     int K, int N,
+                                                                     bf16_t* __restrict__ C, int th) {
   __shared__ __attribute__((aligned(16))) bf16_t As[XG_LDS];
-  __shared__ int pre[XG_MAXN + 1];
-  RowBlock rb = schedule(offsets, e_begin, e_end, nblk_n, th, pre);
+  __shared__ int pre[2 * (XG_MAXN + 1)];
+  // GEMM-1 is counted in weight columns: each workgroup streams WG_H columns of W1 and of W3
+  const int ncols = SWIGLU ? 2 * N : N;
+  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, pre);
   // values from LDS and the wave index are wave-uniform; say so, so that
   // pointers and buffer descriptors built from them live in scalar registers
   rb.e = __builtin_amdgcn_readfirstlane(rb.e);
   rb.r0 = __builtin_amdgcn_readfirstlane(rb.r0);
   rb.R = __builtin_amdgcn_readfirstlane(rb.R);
   rb.nb = __builtin_amdgcn_readfirstlane(rb.nb);
+  rb.cls = __builtin_amdgcn_readfirstlane(rb.cls);
   if (rb.R <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int i = threadIdx.x & 15;
-  int col;
-  const bf16_t* Bl;
-  const int64_t estride = (int64_t)K * N;
-  if (SWIGLU) {  // lower half of the waves streams W1, upper half the same columns of W3
-    col = rb.nb * 128 + (wave % (XG_NW / 2)) * XG_HW + XG_CPL * i;
-    Bl = ((wave < XG_NW / 2) ? B1 : B3) + rb.e * estride;
-  } else {       // output columns per wave
-    col = rb.nb * 256 + wave * XG_OW + XG_CPL * i;
-    Bl = B1 + rb.e * estride;
-  }
-  const int mt = (rb.R + 15) >> 4;
-  switch (mt) {
-#define XG_CASE(n) \
-  case n: gemm_body<SWIGLU, n>(A, Bl, K, N, col, C, rb, As); break;
-    XG_CASE(1) XG_CASE(2) XG_CASE(3) XG_CASE(4) XG_CASE(5)
-    XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
-#undef XG_CASE
-    default: break;
-  }
+  if (rb.cls == 0)
+    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, wave, As);
+  else
+    stream_block<XGWide, SWIGLU>(A, B1, B3, K, N, C, rb, wave, As);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,9 +317,9 @@ struct BigTile {
   int e, r0, R, nt;
 };
 
-__device__ BigTile schedule_big(const int32_t* __restrict__ offsets, int e_begin, int e_end,
-                                int ntn, int* pre) {
-  const int ne = e_end - e_begin;
+// pre[j] = inclusive prefix of the m-tiles of the experts with at least XB_TH
+// rows; returns the total.  All threads call; wave 0 scans.
+__device__ int big_prefix(const int32_t* __restrict__ offsets, int e_begin, int ne, int* pre) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int carry = 0;
@@ -267,14 +339,14 @@ __device__ BigTile schedule_big(const int32_t* __restrict__ offsets, int e_begin
     if (lane == 0) pre[XG_MAXN] = carry;
   }
   __syncthreads();
-  BigTile bt{0, 0, 0, 0};
-  const int tot_m = pre[XG_MAXN];
-  const int G = tot_m * ntn;
-  const int b = blockIdx.x;
-  if (b >= G) return bt;
-  const int xcd = b & 7, q = b >> 3;
-  const int L = xcd * (G >> 3) + min(xcd, G & 7) + q;
-  // groups of XB_GM m-tiles; inside a group the m-tile index runs fastest
+  return pre[XG_MAXN];
+}
+
+// Tile L of tot_m * ntn: groups of XB_GM m-tiles, inside a group the m-tile
+// index runs fastest, so consecutive tiles share weight columns.
+__device__ BigTile big_tile_at(int L, const int32_t* __restrict__ offsets, int e_begin, int ne,
+                               int ntn, int tot_m, const int* pre) {
+  BigTile bt;
   const int mg = L / (XB_GM * ntn);
   const int rem = L - mg * XB_GM * ntn;
   const int gsz = min(XB_GM, tot_m - mg * XB_GM);
@@ -380,19 +452,10 @@ __device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs, 
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
 // K and N tails are bounded by the buffer descriptors.
 template <bool SWIGLU>
-__global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int e_begin, int e_end,
-    const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3, int K, int N,
-    bf16_t* __restrict__ C, int ntn) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
-  __shared__ int pre[XG_MAXN + 1];
-  BigTile bt = schedule_big(offsets, e_begin, e_end, ntn, pre);
-  bt.e = __builtin_amdgcn_readfirstlane(bt.e);
-  bt.r0 = __builtin_amdgcn_readfirstlane(bt.r0);
-  bt.R = __builtin_amdgcn_readfirstlane(bt.R);
-  bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
-  if (bt.R <= 0) return;
+__device__ __forceinline__ void big_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
+                                         const bf16_t* __restrict__ B3, int K, int N,
+                                         bf16_t* __restrict__ C, const BigTile& bt,
+                                         bf16_t (*As)[XB_BM * GC_LDA], bf16_t (*Bs)[XB_BN * GC_LDA]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t estride = (int64_t)K * N;
@@ -472,6 +535,51 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
   }
 }
 
+// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
+// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
+// K and N tails are bounded by the buffer descriptors.
+//
+// The tile order is cut into 8 contiguous ranges, one per XCD (workgroup id
+// mod 8 on this part); workgroup (x, q) of the G = gridDim.x takes tiles
+// q, q + G/8, ... of range x, so the tiles of a range start in order and
+// neighbouring tiles share operands in that XCD's L2.  With G at least 8 times
+// the largest range every workgroup takes at most one tile and the hardware
+// balances the compute units; a smaller G makes the launch cheap when there are
+// few or no large segments.
+template <bool SWIGLU>
+__global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
+    const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int e_begin, int e_end,
+    const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3, int K, int N,
+    bf16_t* __restrict__ C, int ntn) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
+  __shared__ int pre[XG_MAXN + 1];
+  const int ne = e_end - e_begin;
+  const int tot_m = big_prefix(offsets, e_begin, ne, pre);
+  const int TT = tot_m * ntn;
+  const int G = gridDim.x;
+  int L, step, end;
+  if ((G & 7) == 0) {
+    const int x = blockIdx.x & 7;
+    L = x * (TT >> 3) + min(x, TT & 7);
+    end = L + (TT >> 3) + (x < (TT & 7) ? 1 : 0);
+    L += blockIdx.x >> 3;
+    step = G >> 3;
+  } else {
+    L = blockIdx.x;
+    end = TT;
+    step = G;
+  }
+  for (; L < end; L += step) {
+    BigTile bt = big_tile_at(L, offsets, e_begin, ne, ntn, tot_m, pre);
+    bt.e = __builtin_amdgcn_readfirstlane(bt.e);
+    bt.r0 = __builtin_amdgcn_readfirstlane(bt.r0);
+    bt.R = __builtin_amdgcn_readfirstlane(bt.R);
+    bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
+    big_tile<SWIGLU>(A, B1, B3, K, N, C, bt, As, Bs);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32: one thread per output element
 // ---------------------------------------------------------------------------
@@ -501,6 +609,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
   C[p * N + n] = SWIGLU ? s1 / (1.0f + expf(-s1)) * s3 : s1;
 }
 
+// Compute units of the current device.
+static int big_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int* c = dev < 64 ? &cache[dev] : nullptr;
+  if (c && *c) return *c;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (c) *c = n;
+  return n;
+}
+
 size_t expert_gemm_ws_bytes(const Prob&) { return 0; }
 
 hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
@@ -512,34 +634,56 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // exceed T rows (top-k picks distinct experts), so small T never needs it
     const bool big = p.T >= XB_TH;
     const int th = big ? XB_TH : INT32_MAX;
-    const int64_t mblocks = (p.rows_max + XG_BM - 1) / XG_BM + (e_end - e_begin);
-    const int64_t bblocks = (p.rows_max + XB_BM - 1) / XB_BM + (e_end - e_begin);
+    const int ne = e_end - e_begin;
+    // Streaming grid: the total work W of schedule().  A thin expert is one
+    // row block of nt blocks of weight XG_WT_THIN, a wide one ceil(cnt / BM)
+    // row blocks of nw blocks of weight 1; a streamed expert has fewer than
+    // min(T + 1, th) rows, and the local row counts add up to at most
+    // rows_max.  Each XCD's share of the blocks is at most ceil(W / 8).
+    const int64_t rbmax = (std::min<int64_t>(p.T, (int64_t)th - 1) + XGWide::BM - 1) / XGWide::BM;
+    auto grid = [&](int ncols) {
+      const int64_t nt = (ncols + XGThin::COLS - 1) / XGThin::COLS;
+      const int64_t nw = (ncols + XGWide::COLS - 1) / XGWide::COLS;
+      const int64_t per_e = std::max<int64_t>(XG_WT_THIN * nt, nw);
+      const int64_t w_rows = ne * per_e + (p.rows_max * nw + XGWide::BM - 1) / XGWide::BM;
+      const int64_t w_exp = ne * std::max<int64_t>(XG_WT_THIN * nt, rbmax * nw);
+      const int64_t w = std::min(w_rows, w_exp);
+      return (unsigned)(8 * ((w + 7) / 8));
+    };
+    // Large-tile grid.  Its tiles: sum over experts with n_e >= XB_TH of
+    // ceil(n_e / BM) <= rows_max / BM + min(ne, rows_max / XB_TH) m-tiles, times
+    // ntn.  When the mean segment reaches XB_TH rows (dense-like routing) the
+    // grid covers every tile with its own workgroup; otherwise there are few
+    // or no large segments and at most 4 workgroups per compute unit loop over
+    // them, which keeps an empty launch short.
+    const int64_t bblocks = (p.rows_max + XB_BM - 1) / XB_BM + std::min<int64_t>(ne, p.rows_max / XB_TH);
+    const bool dense_like = (int64_t)p.T * p.k >= (int64_t)XB_TH * p.E;
+    auto big_grid = [&](int ntn) {
+      const int64_t w = bblocks * ntn;
+      return (unsigned)(dense_like ? w : std::min<int64_t>(w, 4 * (int64_t)big_cus()));
+    };
     hipError_t e;
-    // GEMM-1 (SwiGLU)
     if (big) {
       const int ntn = (p.f + 127) / 128;
-      hipLaunchKernelGGL(grouped_gemm_bf16_big<true>, dim3((unsigned)(bblocks * ntn)), dim3(64 * XB_NW), 0, st,
+      hipLaunchKernelGGL(grouped_gemm_bf16_big<true>, dim3(big_grid(ntn)), dim3(64 * XB_NW), 0, st,
                          (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
                          (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int nb1 = (p.f + 127) / 128;
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3((unsigned)(mblocks * nb1)), dim3(64 * XG_NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f)), dim3(64 * XGWide::NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, nb1, th);
+                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // GEMM-2 (down projection)
     if (big) {
       const int ntn = (p.d + 255) / 256;
-      hipLaunchKernelGGL(grouped_gemm_bf16_big<false>, dim3((unsigned)(bblocks * ntn)), dim3(64 * XB_NW), 0, st, (const bf16_t*)h,
-                         offsets, e_begin, e_end, (const bf16_t*)w2, (const bf16_t*)nullptr, p.f,
-                         p.d, (bf16_t*)y_packed, ntn);
+      hipLaunchKernelGGL(grouped_gemm_bf16_big<false>, dim3(big_grid(ntn)), dim3(64 * XB_NW), 0, st,
+                         (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
+                         (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, ntn);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int nb2 = (p.d + 255) / 256;
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3((unsigned)(mblocks * nb2)), dim3(64 * XG_NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d)), dim3(64 * XGWide::NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, nb2, th);
+                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th);
     return hipGetLastError();
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);

@@ -34,7 +34,7 @@ namespace moe {
 
 constexpr int GC_KS = 64;            // K per stage
 constexpr int GC_LDA = GC_KS + 8;    // LDS row stride in bf16 (144 B): fragment reads hit distinct banks
-constexpr int GC_NBUF = 3;           // register ring depth
+constexpr int GC_NBUF = 3;           // default register ring depth
 constexpr uint32_t GC_RSRC_W3 = 0x00020000u;  // buffer descriptor word 3 for gfx9-family raw buffers
 constexpr uint32_t GC_OOR = 0x80000000u;      // lane offset that is outside every descriptor
 
@@ -54,13 +54,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gc_rsrc(const void* base, uint
                                            (int)GC_RSRC_W3);
 }
 
-template <int NW, int CPL, int MT>
+template <int NW, int CPL, int MT, int NB = GC_NBUF>
 struct Pipe {
+  static constexpr int NBUF = NB;                          // register ring slots
   static constexpr int NT = 64 * NW;                       // threads
   static constexpr int AV = (128 * MT + NT - 1) / NT;      // 16-byte A vectors per thread per stage
   static constexpr int AROWS = AV * NT / 8;                // rows per LDS stage buffer
-  BBlk<CPL> b[GC_NBUF][2];
-  u32x4 ar[GC_NBUF][AV];
+  BBlk<CPL> b[NB][2];
+  u32x4 ar[NB][AV];
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va[AV];   // per-lane A offsets (bytes), fixed for the loop
   uint32_t vb;       // per-lane B offset (bytes), fixed for the loop
@@ -70,14 +71,14 @@ struct Pipe {
 template <int NW, int CPL, int MT>
 constexpr int gc_lds_elems() { return 2 * Pipe<NW, CPL, MT>::AROWS * GC_LDA; }
 
-template <int NW, int CPL, int MT>
-__device__ __forceinline__ void gc_setup(Pipe<NW, CPL, MT>& P, const GemmArgs& g) {
+template <int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_setup(Pipe<NW, CPL, MT, NB>& P, const GemmArgs& g) {
   // A descriptor spans the block's rows; B descriptor spans rows [0, kend).
   P.ra = gc_rsrc(g.A, (uint32_t)((int64_t)g.R * g.lda * 2));
   P.rb = gc_rsrc(g.B, (uint32_t)((int64_t)g.kend * g.ldb * 2));
 #pragma unroll
-  for (int q = 0; q < Pipe<NW, CPL, MT>::AV; ++q) {
-    const int v = threadIdx.x + Pipe<NW, CPL, MT>::NT * q;
+  for (int q = 0; q < Pipe<NW, CPL, MT, NB>::AV; ++q) {
+    const int v = threadIdx.x + Pipe<NW, CPL, MT, NB>::NT * q;
     const int r = min(v >> 3, g.R - 1);
     P.va[q] = (uint32_t)(((int64_t)r * g.lda + 8 * (v & 7)) * 2);
   }
@@ -85,8 +86,8 @@ __device__ __forceinline__ void gc_setup(Pipe<NW, CPL, MT>& P, const GemmArgs& g
   P.vb = g.col < g.N ? (uint32_t)(((int64_t)(8 * grp) * g.ldb + g.col) * 2) : GC_OOR;
 }
 
-template <int J, int NW, int CPL, int MT>
-__device__ __forceinline__ void gc_issue(Pipe<NW, CPL, MT>& P, int st, const GemmArgs& g) {
+template <int J, int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_issue(Pipe<NW, CPL, MT, NB>& P, int st, const GemmArgs& g) {
   const int k0 = g.kbeg + st * GC_KS;
   const uint32_t row_bytes = (uint32_t)(g.ldb * 2);
 #pragma unroll
@@ -101,26 +102,26 @@ __device__ __forceinline__ void gc_issue(Pipe<NW, CPL, MT>& P, int st, const Gem
     }
   }
 #pragma unroll
-  for (int q = 0; q < Pipe<NW, CPL, MT>::AV; ++q)
+  for (int q = 0; q < Pipe<NW, CPL, MT, NB>::AV; ++q)
     P.ar[J][q] = __builtin_amdgcn_raw_buffer_load_b128(P.ra, P.va[q], (uint32_t)(k0 * 2), 0);
 }
 
-template <int J, int NW, int CPL, int MT>
-__device__ __forceinline__ void gc_stash(Pipe<NW, CPL, MT>& P, int st, bf16_t* As) {
-  bf16_t* dst = As + (st & 1) * (Pipe<NW, CPL, MT>::AROWS * GC_LDA);
+template <int J, int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_stash(Pipe<NW, CPL, MT, NB>& P, int st, bf16_t* As) {
+  bf16_t* dst = As + (st & 1) * (Pipe<NW, CPL, MT, NB>::AROWS * GC_LDA);
 #pragma unroll
-  for (int q = 0; q < Pipe<NW, CPL, MT>::AV; ++q) {
-    const int v = threadIdx.x + Pipe<NW, CPL, MT>::NT * q;
+  for (int q = 0; q < Pipe<NW, CPL, MT, NB>::AV; ++q) {
+    const int v = threadIdx.x + Pipe<NW, CPL, MT, NB>::NT * q;
     *reinterpret_cast<u32x4*>(dst + (v >> 3) * GC_LDA + 8 * (v & 7)) = P.ar[J][q];
   }
 }
 
-template <int J, int NW, int CPL, int MT>
-__device__ __forceinline__ void gc_compute(Pipe<NW, CPL, MT>& P, int st, const bf16_t* As,
+template <int J, int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_compute(Pipe<NW, CPL, MT, NB>& P, int st, const bf16_t* As,
                                            f32x4 (&acc)[MT][CPL]) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const bf16_t* src = As + (st & 1) * (Pipe<NW, CPL, MT>::AROWS * GC_LDA) + i * GC_LDA + 8 * g;
+  const bf16_t* src = As + (st & 1) * (Pipe<NW, CPL, MT, NB>::AROWS * GC_LDA) + i * GC_LDA + 8 * g;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     bf16x8 bf[CPL];
@@ -134,27 +135,34 @@ __device__ __forceinline__ void gc_compute(Pipe<NW, CPL, MT>& P, int st, const b
   }
 }
 
-// Stage st uses ring slot J; it refills slot J-1 (consumed by stage st-1)
-// with stage st+2, multiplies, then writes A of stage st+1 into LDS.  GUARD
-// selects the form with range conditions (prologue/tail); the steady-state
-// form has none, so a whole trip of three steps is one basic block and the
-// loads cannot be sunk towards their use two steps later.  The scheduling
-// barrier after the issue keeps the machine scheduler from doing the same.
-template <int J, bool GUARD, int NW, int CPL, int MT>
-__device__ __forceinline__ void gc_step(Pipe<NW, CPL, MT>& P, int st, int nst, const GemmArgs& g,
+// Stage st uses ring slot J = st % NB; it refills the slot consumed by stage
+// st-1 with stage st+NB-1, multiplies, then writes A of stage st+1 into LDS.
+// GUARD selects the form with range conditions (prologue/tail); the
+// steady-state form has none, so a whole trip of NB steps is one basic block
+// and the loads cannot be sunk towards their use.  The scheduling barrier
+// after the issue keeps the machine scheduler from doing the same.
+template <int J, bool GUARD, int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_step(Pipe<NW, CPL, MT, NB>& P, int st, int nst, const GemmArgs& g,
                                         bf16_t* As, f32x4 (&acc)[MT][CPL]) {
   if (GUARD && st >= nst) return;
-  if (!GUARD || st + 2 < nst) gc_issue<(J + 2) % GC_NBUF>(P, st + 2, g);
+  if (!GUARD || st + NB - 1 < nst) gc_issue<(J + NB - 1) % NB>(P, st + NB - 1, g);
   __builtin_amdgcn_sched_barrier(0);
   gc_compute<J>(P, st, As, acc);
-  if (!GUARD || st + 1 < nst) gc_stash<(J + 1) % GC_NBUF>(P, st + 1, As);
+  if (!GUARD || st + 1 < nst) gc_stash<(J + 1) % NB>(P, st + 1, As);
   __syncthreads();
+}
+
+template <int J, bool GUARD, int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_trip(Pipe<NW, CPL, MT, NB>& P, int st, int nst, const GemmArgs& g,
+                                        bf16_t* As, f32x4 (&acc)[MT][CPL]) {
+  gc_step<J, GUARD>(P, st + J, nst, g, As, acc);
+  if constexpr (J + 1 < NB) gc_trip<J + 1, GUARD>(P, st, nst, g, As, acc);
 }
 
 // acc[mt][c][r] receives rows 16 mt + 4 (lane / 16) + r, column g.col + c.
 // As must hold gc_lds_elems<NW, CPL, MT>() bf16; g.R >= 1.  All 64*NW threads
-// must call this.
-template <int NW, int CPL, int MT>
+// must call this.  NB is the register ring depth (stages in flight + 1).
+template <int NW, int CPL, int MT, int NB = GC_NBUF>
 __device__ __forceinline__ void gemm_mainloop(const GemmArgs& g, bf16_t* As,
                                               f32x4 (&acc)[MT][CPL]) {
 #pragma unroll
@@ -163,23 +171,22 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& g, bf16_t* As,
     for (int c = 0; c < CPL; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nst = (g.kend - g.kbeg + GC_KS - 1) / GC_KS;
   if (nst <= 0) return;
-  Pipe<NW, CPL, MT> P;
+  Pipe<NW, CPL, MT, NB> P;
   gc_setup(P, g);
-  gc_issue<0>(P, 0, g);
-  if (nst > 1) gc_issue<1>(P, 1, g);
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (j < nst) {
+      if (j == 0) gc_issue<0>(P, 0, g);
+      if constexpr (NB > 2) { if (j == 1) gc_issue<1 % NB>(P, 1, g); }
+    }
   gc_stash<0>(P, 0, As);
   __syncthreads();
   int st = 0;
-  for (; st + 5 <= nst; st += GC_NBUF) {   // stages st .. st+4 exist
-    gc_step<0, false>(P, st, nst, g, As, acc);
-    gc_step<1, false>(P, st + 1, nst, g, As, acc);
-    gc_step<2, false>(P, st + 2, nst, g, As, acc);
-  }
-  // at most 4 stages remain; the slot of stage st is 0 here
-  gc_step<0, true>(P, st, nst, g, As, acc);
-  gc_step<1, true>(P, st + 1, nst, g, As, acc);
-  gc_step<2, true>(P, st + 2, nst, g, As, acc);
-  gc_step<0, true>(P, st + 3, nst, g, As, acc);
+  for (; st + 2 * NB - 1 <= nst; st += NB)   // stages st .. st + 2 NB - 2 exist
+    gc_trip<0, false>(P, st, nst, g, As, acc);
+  // fewer than 2 NB - 1 stages remain; the slot of stage st is 0 here
+  gc_trip<0, true>(P, st, nst, g, As, acc);
+  gc_trip<0, true>(P, st + NB, nst, g, As, acc);
 }
 
 }  // namespace moe

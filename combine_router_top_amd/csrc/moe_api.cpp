@@ -82,7 +82,7 @@ moe_status_t check_problem(const moe_problem_t* p, moe::Prob* out) {
 
 // Workspace layout of moe_layer (each region 256-byte aligned).
 struct LayerWs {
-  size_t route, idx, w, counts, offsets, perm, inv, disp, xp, h, yp, total;
+  size_t route, idx, w, counts, offsets, perm, inv, disp, xp, h, yp, gemm, total;
 };
 
 LayerWs layer_ws(const moe::Prob& p) {
@@ -105,7 +105,8 @@ LayerWs layer_ws(const moe::Prob& p) {
   L.xp = take((size_t)p.rows_max * p.d * es);
   L.h = take((size_t)p.rows_max * p.f * es);
   L.yp = take((size_t)p.rows_max * p.d * es);
-  L.total = o + moe::expert_gemm_ws_bytes(p);
+  L.gemm = take(moe::expert_gemm_ws_bytes(p));
+  L.total = o;
   return L;
 }
 
@@ -313,7 +314,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   if (!overlap) {
     e = moe::launch_gather(q, x, offsets, perm, xp, 0, q.n, s0);
     if (e == hipSuccess)
-      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.total, 0, q.n, s0);
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0);
   } else {
     // two-stream dispatch overlap: the upper half of the local experts is
     // packed on s1 while the lower half's GEMMs run on s0.
@@ -325,10 +326,10 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
     if (e == hipSuccess) e = hipEventRecord(g_ev.b, s1);
     if (e == hipSuccess) e = moe::launch_gather(q, x, offsets, perm, xp, 0, half, s0);
     if (e == hipSuccess)
-      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.total, 0, half, s0);
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, half, s0);
     if (e == hipSuccess) e = hipStreamWaitEvent(s0, g_ev.b, 0);
     if (e == hipSuccess)
-      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.total, half, q.n, s0);
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, half, q.n, s0);
   }
   if (e == hipSuccess) e = moe::launch_combine(q, yp, inv, w, y, s0);
   return hip_status(e, "moe_layer");

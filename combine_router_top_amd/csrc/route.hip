@@ -7,12 +7,13 @@
 //
 // Kernels
 //   router_wide_mfma    bf16, E % 4 == 0 and E > 16: split-K MFMA GEMM on the
-//                       pipelined core (gemm_core.h); each wave owns 64
-//                       expert columns, the workgroup 64 tokens and 256
-//                       experts.  Writes fp32 partial sums per K split.
+//                       pipelined core (gemm_core.h); 8 waves, each 160
+//                       tokens x 32 experts, the workgroup 160 x 256.  Writes
+//                       fp32 partial sums per K split.
 //   router_narrow_mfma  bf16, E <= 16 and E*d <= 32K: W_g^T staged once in LDS,
-//                       each wave streams its own 32 token rows straight from
-//                       HBM into MFMA A fragments.  HBM-bound on x.
+//                       each wave streams its own 32 token rows with buffer
+//                       loads straight into MFMA A fragments, one 128-K chunk
+//                       in flight.  HBM-bound on x.
 //   router_plain        any dtype/shape: one thread per logit (fp32 problems
 //                       and shapes the MFMA kernels do not cover).
 //   topk_softmax_kernel one wave per token: sums the K splits in fixed order,
@@ -27,35 +28,40 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // wide router (bf16, MFMA, split-K) on the pipelined core of gemm_core.h
 // ---------------------------------------------------------------------------
-constexpr int RW_MT = 4;        // m-tiles per workgroup
+// 160 tokens x 256 experts per workgroup (8 waves, each 160 x 32), so that the
+// gate matrix is re-read once per 160 tokens; K is split to fill the chip.
+constexpr int RW_NW = 8;
+constexpr int RW_CPL = 2;
+constexpr int RW_MT = 10;          // m-tiles per workgroup
 constexpr int RW_BM = 16 * RW_MT;  // tokens per workgroup
-constexpr int RW_BN = 256;      // experts per workgroup (4 waves x 64)
+constexpr int RW_BN = 256;         // experts per workgroup (8 waves x 32)
 
-__global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict__ x,
-                                                        const bf16_t* __restrict__ wg,
-                                                        float* __restrict__ part, int T, int d,
-                                                        int E, int kchunk) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<4, 4, RW_MT>()];
+__global__ __launch_bounds__(64 * RW_NW) void router_wide_mfma(const bf16_t* __restrict__ x,
+                                                               const bf16_t* __restrict__ wg,
+                                                               float* __restrict__ part, int T,
+                                                               int d, int E, int kchunk) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<RW_NW, RW_CPL, RW_MT>()];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, g = lane >> 4;
   const int m0 = blockIdx.x * RW_BM;
   const int split = blockIdx.y;
   const int kbeg = split * kchunk;
   const int kend = min(d, kbeg + kchunk);
-  const int col = blockIdx.z * RW_BN + wave * 64 + 4 * i;
-  GemmArgs ga{x + (int64_t)m0 * d, d, min(RW_BM, T - m0), wg, E, kbeg, kend, E, col};
-  f32x4 acc[RW_MT][4];
-  gemm_mainloop<4, 4, RW_MT>(ga, As, acc);
+  const int col = blockIdx.z * RW_BN + wave * 16 * RW_CPL + RW_CPL * i;
+  const int R = min(RW_BM, T - m0);
+  GemmArgs ga{x + (int64_t)m0 * d, d, R, wg, E, kbeg, kend, E, col};
+  f32x4 acc[RW_MT][RW_CPL];
+  gemm_mainloop<RW_NW, RW_CPL, RW_MT>(ga, As, acc);
   if (col >= E) return;
   float* out = part + (int64_t)split * T * E;
 #pragma unroll
   for (int mt = 0; mt < RW_MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + 16 * mt + 4 * g + r;
-      if (row < T) {
-        f32x4 v = f32x4{acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
-        *reinterpret_cast<f32x4*>(out + (int64_t)row * E + col) = v;
+      const int row = 16 * mt + 4 * g + r;
+      if (row < R) {
+        f32x2 v = f32x2{acc[mt][0][r], acc[mt][1][r]};
+        *reinterpret_cast<f32x2*>(out + (int64_t)(m0 + row) * E + col) = v;
       }
     }
 }
@@ -63,8 +69,41 @@ __global__ __launch_bounds__(256) void router_wide_mfma(const bf16_t* __restrict
 // ---------------------------------------------------------------------------
 // narrow router (bf16, MFMA, E <= 16)
 // ---------------------------------------------------------------------------
-constexpr int RN_MT = 2;        // m-tiles per wave (32 tokens)
+// W_g^T is staged once per workgroup in LDS; each wave streams its own 32
+// token rows with buffer loads (fixed lane offsets, scalar K offsets) straight
+// into MFMA A fragments, 128 of K per chunk with the next chunk in flight.
+// Rows past T and K past d read zeros (descriptor bounds / zero B fragments).
+constexpr int RN_MT = 1;                 // m-tiles per wave (16 tokens)
 constexpr int RN_ROWS = 4 * 16 * RN_MT;  // tokens per workgroup
+constexpr int RN_KC = 256;               // K per chunk (8 MFMA k-steps)
+
+struct NarrowChunk {
+  u32x4 a[RN_MT][RN_KC / 32];
+};
+
+__device__ __forceinline__ void rn_issue(NarrowChunk& c, __amdgpu_buffer_rsrc_t rs,
+                                         const uint32_t (&voff)[RN_MT], int k0) {
+#pragma unroll
+  for (int u = 0; u < RN_KC / 32; ++u)
+#pragma unroll
+    for (int mt = 0; mt < RN_MT; ++mt)
+      c.a[mt][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[mt], (uint32_t)((k0 + 32 * u) * 2), 0);
+}
+
+__device__ __forceinline__ void rn_compute(const NarrowChunk& c, const bf16_t* WgT, int d, int E,
+                                           int k0, f32x4 (&acc)[RN_MT]) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < RN_KC / 32; ++u) {
+    const int k = k0 + 32 * u + 8 * g;
+    bf16x8 bfr = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    if (i < E && k < d) bfr = *reinterpret_cast<const bf16x8*>(WgT + i * d + k);
+#pragma unroll
+    for (int mt = 0; mt < RN_MT; ++mt)
+      acc[mt] = mfma16(__builtin_bit_cast(bf16x8, c.a[mt][u]), bfr, acc[mt]);
+  }
+}
 
 __global__ __launch_bounds__(256) void router_narrow_mfma(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wg,
@@ -72,47 +111,70 @@ __global__ __launch_bounds__(256) void router_narrow_mfma(const bf16_t* __restri
                                                           int d, int E) {
   extern __shared__ __attribute__((aligned(16))) bf16_t WgT[];  // [E][d]
   const int tid = threadIdx.x;
-  // W_g is [d][E] row-major; read it in 16-byte pieces and scatter transposed.
-  for (int v = tid; v < (E * d) >> 3; v += 256) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(wg + 8 * (int64_t)v);
+  // W_g is [d][E] row-major.  With E a multiple of 8 each thread takes 8 rows
+  // x 8 experts, transposes the 8 x 8 block in registers and writes 8 x 16
+  // bytes; otherwise it scatters 2-byte elements.
+  if ((E & 7) == 0) {
+    const int ng = E >> 3;
+    for (int v = tid; v < (d >> 3) * ng; v += 256) {
+      const int kg = v / ng, eg = v - kg * ng;
+      u32x4 rowv[8];
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const int flat = 8 * v + h;
-      const int kk = flat / E, e = flat - kk * E;
-      WgT[e * d + kk] = (bf16_t)((h & 1) ? (q[h >> 1] >> 16) : (q[h >> 1] & 0xFFFFu));
+      for (int r = 0; r < 8; ++r)
+        rowv[r] = *reinterpret_cast<const u32x4*>(wg + (int64_t)(8 * kg + r) * E + 8 * eg);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = __builtin_amdgcn_perm(rowv[2 * q + 1][c >> 1], rowv[2 * q][c >> 1], sel);
+        *reinterpret_cast<u32x4*>(WgT + (8 * eg + c) * d + 8 * kg) = o;
+      }
+    }
+  } else {
+    for (int v = tid; v < (E * d) >> 3; v += 256) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(wg + 8 * (int64_t)v);
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const int flat = 8 * v + h;
+        const int kk = flat / E, e = flat - kk * E;
+        WgT[e * d + kk] = (bf16_t)((h & 1) ? (q[h >> 1] >> 16) : (q[h >> 1] & 0xFFFFu));
+      }
     }
   }
   __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int m0 = blockIdx.x * RN_ROWS + wave * 16 * RN_MT;
+  const int R = min(16 * RN_MT, T - m0);
+  if (R <= 0) return;
+  const __amdgpu_buffer_rsrc_t rs = gc_rsrc(x + (int64_t)m0 * d, (uint32_t)((int64_t)R * d * 2));
+  uint32_t voff[RN_MT];
+#pragma unroll
+  for (int mt = 0; mt < RN_MT; ++mt) {
+    const int r = 16 * mt + i;
+    voff[mt] = r < R ? (uint32_t)(((int64_t)r * d + 8 * g) * 2) : GC_OOR;
+  }
   f32x4 acc[RN_MT];
 #pragma unroll
   for (int a = 0; a < RN_MT; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool colok = i < E;
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const int k = k0 + 8 * g;
-    bf16x8 bfr;
-    if (colok && k < d) {
-      bfr = *reinterpret_cast<const bf16x8*>(WgT + i * d + k);
-    } else {
-      bfr = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
-#pragma unroll
-    for (int mt = 0; mt < RN_MT; ++mt) {
-      const int row = m0 + 16 * mt + i;
-      u32x4 a = u32x4{0u, 0u, 0u, 0u};
-      if (row < T && k < d) a = *reinterpret_cast<const u32x4*>(x + (int64_t)row * d + k);
-      acc[mt] = mfma16(__builtin_bit_cast(bf16x8, a), bfr, acc[mt]);
-    }
+  NarrowChunk c0, c1;
+  rn_issue(c0, rs, voff, 0);
+  for (int k0 = 0; k0 < d; k0 += 2 * RN_KC) {
+    if (k0 + RN_KC < d) rn_issue(c1, rs, voff, k0 + RN_KC);
+    rn_compute(c0, WgT, d, E, k0, acc);
+    if (k0 + RN_KC >= d) break;
+    if (k0 + 2 * RN_KC < d) rn_issue(c0, rs, voff, k0 + 2 * RN_KC);
+    rn_compute(c1, WgT, d, E, k0 + RN_KC, acc);
   }
-  if (!colok) return;
+  if (i >= E) return;
 #pragma unroll
   for (int mt = 0; mt < RN_MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + 16 * mt + 4 * g + r;
-      if (row < T) logits[(int64_t)row * E + i] = acc[mt][r];
+      const int row = 16 * mt + 4 * g + r;
+      if (row < R) logits[(int64_t)(m0 + row) * E + i] = acc[mt][r];
     }
 }
 
@@ -206,8 +268,19 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     key[j] = 0;
     const int e = lane + 64 * j;
     if (e < E) {
-      float v = part[(int64_t)t * E + e];
-      for (int s = 1; s < nsplit; ++s) v += part[((int64_t)s * T + t) * E + e];
+      // sum the K splits in ascending order; loads issued 8 at a time
+      const float* pe = part + (int64_t)t * E + e;
+      const int64_t sstride = (int64_t)T * E;
+      float v = pe[0];
+      int s = 1;
+      for (; s + 8 <= nsplit; s += 8) {
+        float q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = pe[(int64_t)(s + u) * sstride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += q[u];
+      }
+      for (; s < nsplit; ++s) v += pe[(int64_t)s * sstride];
       if (bias) v += bias[e];
       if (logits_out) logits_out[(int64_t)t * E + e] = v;
       key[j] = ((uint64_t)f32_order_key(v) << 32) | (uint32_t)(1023 - e);
@@ -254,7 +327,7 @@ static RouteKind route_kind(const Prob& p) {
 
 static int route_splits(const Prob& p) {
   if (route_kind(p) != ROUTE_WIDE) return 1;
-  // enough workgroups to cover the chip, every split keeps >= 256 of K
+  // about 256 workgroups over the chip, every split keeps >= 256 of K
   const int64_t blocks = (int64_t)((p.T + RW_BM - 1) / RW_BM) * ((p.E + RW_BN - 1) / RW_BN);
   int64_t s = (256 + blocks - 1) / blocks;
   const int64_t smax = p.d / 256 > 1 ? p.d / 256 : 1;
@@ -280,7 +353,7 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
   if (kind == ROUTE_WIDE) {
     const int kchunk = route_kchunk(p, S);
     dim3 grid((p.T + RW_BM - 1) / RW_BM, S, (p.E + RW_BN - 1) / RW_BN);
-    hipLaunchKernelGGL(router_wide_mfma, grid, dim3(256), 0, st, (const bf16_t*)x, (const bf16_t*)wg, part, p.T,
+    hipLaunchKernelGGL(router_wide_mfma, grid, dim3(64 * RW_NW), 0, st, (const bf16_t*)x, (const bf16_t*)wg, part, p.T,
                        p.d, p.E, kchunk);
   } else if (kind == ROUTE_NARROW) {
     dim3 grid((p.T + RN_ROWS - 1) / RN_ROWS);

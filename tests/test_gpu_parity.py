@@ -33,6 +33,8 @@ SMALL = {
     "big_tails": W("big_tails", 1500, 328, 4, 2, 264, 0, 4, "bf16", seed=14),
     # skewed: some experts on the large-tile kernel, the rest streamed
     "big_mixed": W("big_mixed", 1200, 256, 16, 4, 256, 0, 8, "bf16", skew=True, seed=15),
+    # all three tile classes (thin <= 48 rows, wide, large >= 320) with column tails
+    "mixed_classes": W("mixed_classes", 700, 264, 24, 4, 328, 0, 12, "bf16", skew=True, seed=16),
 }
 
 _cache = {}
