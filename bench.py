@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense flop/s
 METRIC = "MoE layer tokens/s on 1 MI355X; grouped-GEMM % MFMA peak, dispatch % HBM"
-GEMM_SOURCES = ["expert_gemm.hip", "mfma_tile.h", "common.h"]
+GEMM_SOURCES = ["expert_gemm.hip", "gemm_core.h", "mfma_tile.h", "common.h"]
 
 
 def parse():
@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy that measures practical HBM bandwidth")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no benchmark: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
+                         "then WRITE_SIZE, --output-format csv) into "
+                         "profiles/traffic_expert_gemm_<workload>.json")
     return ap.parse_args()
 
 
@@ -70,6 +74,53 @@ def committed_traffic(workload: str):
     if t.get("source_hash") != gemm_source_hash():
         return None
     return t.get("hbm_bytes_per_call")
+
+
+def _pmc_rows(d):
+    """(kernel name, counter value in KiB) per dispatch from a rocprofv3 csv run."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(paths[0]) as fh:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(fh)]
+
+
+def write_traffic(a):
+    """HBM bytes per moe_expert_gemm call from FETCH_SIZE and WRITE_SIZE runs.
+    Each counter is scaled by bytes-moved / counter for the device copy of
+    --copy-gib GiB recorded in the same run (it reads and writes that many
+    bytes); the call's launches (SwiGLU GEMM-1, down GEMM-2 and, when launched,
+    the two large-tile launches) each run once per call."""
+    n = a.copy_gib * (1 << 30)
+    res = {}
+    for cname, d in (("FETCH_SIZE", a.write_traffic[0]), ("WRITE_SIZE", a.write_traffic[1])):
+        rows = _pmc_rows(d)
+        copies = [v for k, v in rows if "copyBuffer" in k]
+        if not copies:
+            raise SystemExit(f"{d}: no device copy dispatch to calibrate {cname}")
+        scale = n / (max(copies) * 1024.0)
+        per = {}
+        for k, v in rows:
+            if "grouped_gemm_bf16" in k:
+                per.setdefault(k.split("(")[0], []).append(v * 1024.0)
+        if not per:
+            raise SystemExit(f"{d}: no grouped GEMM dispatches")
+        raw = sum(sum(v) / len(v) for v in per.values())
+        res[cname] = {"scale": scale, "raw_bytes_per_call": raw, "bytes_per_call": raw * scale,
+                      "dispatches": {k: len(v) for k, v in per.items()}}
+    out = {"workload": a.workload, "source_hash": gemm_source_hash(),
+           "hbm_bytes_per_call": res["FETCH_SIZE"]["bytes_per_call"] + res["WRITE_SIZE"]["bytes_per_call"],
+           "counters": res,
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py "
+                        f"--workload {a.workload} --steps 3 --warmup 1 --no-cpu-baseline"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    path = os.path.join(ROOT, "profiles", f"traffic_expert_gemm_{a.workload}.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 def work_model(w, A, active, s):
@@ -150,6 +201,9 @@ def cpu_baseline(w, inp, budget):
 
 def main():
     a = parse()
+    if a.write_traffic:
+        write_traffic(a)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}, "
@@ -252,7 +306,8 @@ def main():
 
     g = phases["expert_gemm"]
     roof = {k: g[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roof["kernel"] = "moe_expert_gemm (grouped_gemm_bf16<SwiGLU> + grouped_gemm_bf16<down>)"
+    roof["kernel"] = ("moe_expert_gemm: grouped_gemm_bf16<SwiGLU> + grouped_gemm_bf16<down> "
+                      "(+ the two large-tile launches when segments reach 320 rows)")
     roof["traffic"] = committed_traffic(w.name)
     roof["algorithmic_bytes"] = model["expert_gemm"]["bytes"]
     roof["algorithmic_flops"] = model["expert_gemm"]["flops"]
