@@ -19,12 +19,12 @@
 // descriptor; they only meet zero weights or land in accumulator rows that are
 // never stored.
 //
-// Pipeline: K advances in stages of 64.  A ring of 3 register slots holds, per
+// Pipeline: K advances in stages of 64.  A ring of NB register slots holds, per
 // stage, the lane's two 8 x CPL weight blocks and its share of the A tile.
-// While stage s is multiplied, stages s+1 and s+2 are in flight.  Loads retire
-// in order, so A and B of a stage are issued together: when A of stage s+1 is
-// written to LDS at the end of stage s, B of stage s+1 has arrived as well and
-// the two newer stages stay outstanding.  One barrier per stage.
+// While stage s is multiplied, stages s+1 .. s+NB-1 are in flight.  Loads
+// retire in order, so A and B of a stage are issued together: when A of stage
+// s+1 is written to LDS at the end of stage s, B of stage s+1 has arrived as
+// well and the newer stages stay outstanding.  One barrier per stage.
 #pragma once
 
 #include "common.h"
@@ -159,6 +159,15 @@ __device__ __forceinline__ void gc_trip(Pipe<NW, CPL, MT, NB>& P, int st, int ns
   if constexpr (J + 1 < NB) gc_trip<J + 1, GUARD>(P, st, nst, g, As, acc);
 }
 
+// Issue stage J into slot J for J = 0 .. NB - 2 (those that exist).
+template <int J, int NW, int CPL, int MT, int NB>
+__device__ __forceinline__ void gc_prologue(Pipe<NW, CPL, MT, NB>& P, int nst, const GemmArgs& g) {
+  if constexpr (J < NB - 1) {
+    if (J < nst) gc_issue<J>(P, J, g);
+    gc_prologue<J + 1>(P, nst, g);
+  }
+}
+
 // acc[mt][c][r] receives rows 16 mt + 4 (lane / 16) + r, column g.col + c.
 // As must hold gc_lds_elems<NW, CPL, MT>() bf16; g.R >= 1.  All 64*NW threads
 // must call this.  NB is the register ring depth (stages in flight + 1).
@@ -173,12 +182,7 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& g, bf16_t* As,
   if (nst <= 0) return;
   Pipe<NW, CPL, MT, NB> P;
   gc_setup(P, g);
-#pragma unroll
-  for (int j = 0; j < NB - 1; ++j)
-    if (j < nst) {
-      if (j == 0) gc_issue<0>(P, 0, g);
-      if constexpr (NB > 2) { if (j == 1) gc_issue<1 % NB>(P, 1, g); }
-    }
+  gc_prologue<0>(P, nst, g);  // stages 0 .. NB - 2 into slots 0 .. NB - 2
   gc_stash<0>(P, 0, As);
   __syncthreads();
   int st = 0;
