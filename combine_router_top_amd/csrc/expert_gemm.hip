@@ -62,8 +62,11 @@ struct XGCfg {
   static constexpr int LDS = gc_lds_elems<NW, CPL, MTMAX>() > 2 * XCH
                                  ? gc_lds_elems<NW, CPL, MTMAX>() : 2 * XCH;
 };
-using XGWide = XGCfg<8, 2, 10, 3>;
 using XGThin = XGCfg<8, 4, 5, 2>;
+// Medium class (more than XG_THIN_MAX rows): blocks of up to XM_BM rows and
+// XM_COLS weight columns (mid_block below).
+constexpr int XM_BM = 192;
+constexpr int XM_COLS = 256;
 
 // Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb,
 // tile class (0: thin, 1: wide).
@@ -81,14 +84,14 @@ constexpr int XG_THIN_MAX = MOE_XG_THIN_MAX;
 static_assert(XG_THIN_MAX <= XGThin::BM, "a thin segment is one row block");
 // Work of a block in units of a wide block: the path is bound by the weight
 // stream, which grows with the block's column count.
-constexpr int XG_WT_THIN = XGThin::COLS / XGWide::COLS;
-static_assert(XG_WT_THIN * XGWide::COLS == XGThin::COLS, "thin columns a multiple of wide ones");
+constexpr int XG_WT_THIN = XGThin::COLS / XM_COLS;
+static_assert(XG_WT_THIN * XM_COLS == XGThin::COLS, "thin columns a multiple of medium ones");
 
 // Blocks of class `cls` of one expert with `cnt` rows (0 for the other class).
 __device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls) {
   if (cnt <= 0 || cnt >= th || (cnt <= XG_THIN_MAX ? 0 : 1) != cls) return 0;
   if (cls == 0) return (ncols + XGThin::COLS - 1) / XGThin::COLS;
-  return (cnt + XGWide::BM - 1) / XGWide::BM * ((ncols + XGWide::COLS - 1) / XGWide::COLS);
+  return (cnt + XM_BM - 1) / XM_BM * ((ncols + XM_COLS - 1) / XM_COLS);
 }
 
 // Schedule from `offsets` (computed by every workgroup, a few hundred cycles).
@@ -152,8 +155,8 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   const int local = L - (lo ? P[lo - 1] : 0);
   const int o = offsets[e];
   const int cnt = offsets[e + 1] - o;
-  const int bm = rb.cls ? XGWide::BM : XGThin::BM;
-  const int cols = rb.cls ? XGWide::COLS : XGThin::COLS;
+  const int bm = rb.cls ? XM_BM : XGThin::BM;
+  const int cols = rb.cls ? XM_COLS : XGThin::COLS;
   const int nblk = (ncols + cols - 1) / cols;
   const int jb = local / nblk;
   rb.nb = local - jb * nblk;
@@ -250,43 +253,6 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
 #undef XG_CASE
     default: break;
   }
-}
-
-static_assert(XGThin::NW == XGWide::NW, "one workgroup size for both tile classes");
-static_assert(XGThin::WG_H * 2 == XGThin::COLS && XGWide::WG_H * 2 == XGWide::COLS,
-              "per workgroup: GEMM-1 streams WG_H columns of W1 and of W3, GEMM-2 COLS columns");
-constexpr int XG_LDS = XGThin::LDS > XGWide::LDS ? XGThin::LDS : XGWide::LDS;
-
-// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
-// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
-// Segments with fewer than `th` rows; each picks its tile class by row count.
-// K and N tails are bounded by the buffer descriptors (gemm_core.h).
-template <bool SWIGLU>
-__global__ __launch_bounds__(64 * XGWide::NW) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
-                                                                     const int32_t* __restrict__ offsets,
-                                                                     int e_begin, int e_end,
-                                                                     const bf16_t* __restrict__ B1,
-                                                                     const bf16_t* __restrict__ B3,
-                                                                     int K, int N,
-                                                                     bf16_t* __restrict__ C, int th) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[XG_LDS];
-  __shared__ int pre[2 * (XG_MAXN + 1)];
-  // GEMM-1 is counted in weight columns: each workgroup streams WG_H columns of W1 and of W3
-  const int ncols = SWIGLU ? 2 * N : N;
-  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, pre);
-  // values from LDS and the wave index are wave-uniform; say so, so that
-  // pointers and buffer descriptors built from them live in scalar registers
-  rb.e = __builtin_amdgcn_readfirstlane(rb.e);
-  rb.r0 = __builtin_amdgcn_readfirstlane(rb.r0);
-  rb.R = __builtin_amdgcn_readfirstlane(rb.R);
-  rb.nb = __builtin_amdgcn_readfirstlane(rb.nb);
-  rb.cls = __builtin_amdgcn_readfirstlane(rb.cls);
-  if (rb.R <= 0) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (rb.cls == 0)
-    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, wave, As);
-  else
-    stream_block<XGWide, SWIGLU>(A, B1, B3, K, N, C, rb, wave, As);
 }
 
 // ---------------------------------------------------------------------------
@@ -445,6 +411,231 @@ __device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs, 
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// medium segments: up to 192 rows x 256 weight columns, both operands via LDS
+// ---------------------------------------------------------------------------
+// A workgroup streams one 256-column weight block of one expert for a block of
+// up to XM_BM rows.  Each thread loads one 8 x 4 block of the 64-K weight stage
+// (32 or 64 lanes side by side along a weight row, so every load instruction
+// reads 256- or 512-byte runs of a row; 4-byte loads of 64-byte runs cap a
+// compute unit near 28 GB/s on this part) and its share of the A rows, both
+// with buffer loads, in a 3-slot register ring (two stages in flight); at the
+// end of a stage the next stage's A rows and transposed weight block are
+// written to the other LDS buffer (same B^T layout as the large tiles).  The 8
+// waves form 2 row halves x 4 column slabs: wave (wm, wn) computes rows
+// 16 MT wm .. + 16 MT - 1 against B^T rows 64 wn .. 64 wn + 63, MT = ceil(R / 32)
+// m-tiles, so each wave reads only its half of the A tile from LDS.
+constexpr int XM_NB = 3;
+constexpr int XM_LDS = 2 * (XM_BM + XB_BN) * GC_LDA;  // bf16: double-buffered A and B^T stages
+static_assert(XM_COLS == XB_BN, "medium blocks use the large-tile B^T layout");
+
+template <int MT>
+struct MidPipe {
+  static constexpr int AV = (MT + 1) / 2;   // 32 MT rows, 64 rows per 16-byte vector round
+  struct Slot {
+    u32x4 a[AV];
+    u32x2 b[8];
+  } s[XM_NB];
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[AV];
+  uint32_t vb, ldb2;
+  int kb, nb;
+};
+
+template <int J, int MT>
+__device__ __forceinline__ void mid_issue(MidPipe<MT>& P, int k0) {
+#pragma unroll
+  for (int j = 0; j < MidPipe<MT>::AV; ++j)
+    P.s[J].a[j] = __builtin_amdgcn_raw_buffer_load_b128(P.ra, P.va[j], (uint32_t)(k0 * 2), 0);
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    P.s[J].b[r] = __builtin_amdgcn_raw_buffer_load_b64(P.rb, P.vb, (uint32_t)(k0 + r) * P.ldb2, 0);
+}
+
+template <int J, bool SWIGLU, int MT>
+__device__ __forceinline__ void mid_store(const MidPipe<MT>& P, bf16_t* As, bf16_t* Bs) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < MidPipe<MT>::AV; ++j)
+    *reinterpret_cast<u32x4*>(As + ((t >> 3) + 64 * j) * GC_LDA + 8 * (t & 7)) = P.s[J].a[j];
+#pragma unroll
+  for (int col = 0; col < 4; ++col) {
+    const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = __builtin_amdgcn_perm(P.s[J].b[2 * q + 1][col >> 1], P.s[J].b[2 * q][col >> 1], sel);
+    *reinterpret_cast<u32x4*>(Bs + big_brow<SWIGLU>(P.nb, col) * GC_LDA + 8 * P.kb) = v;
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void mid_compute(const bf16_t* As, const bf16_t* Bs, int wm, int wn,
+                                            f32x4 (&acc)[MT][4]) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const bf16_t* a0 = As + (16 * MT * wm + i) * GC_LDA + 8 * g;
+  const bf16_t* b0 = Bs + (64 * wn + i) * GC_LDA + 8 * g;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    bf16x8 bf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      bf[t] = *reinterpret_cast<const bf16x8*>(b0 + 16 * t * GC_LDA + 32 * sub);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(a0 + 16 * mt * GC_LDA + 32 * sub);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
+    }
+  }
+}
+
+// Stage st in ring slot J = st % XM_NB: refill the slot of stage st - 1 with
+// stage st + 2, multiply stage st, write stage st + 1 into the other LDS
+// buffer, barrier.  GUARD as in gemm_core.h.
+template <int J, bool GUARD, bool SWIGLU, int MT>
+__device__ __forceinline__ void mid_step(MidPipe<MT>& P, int st, int nst, bf16_t* As, bf16_t* Bs,
+                                         f32x4 (&acc)[MT][4], int wm, int wn) {
+  if (GUARD && st >= nst) return;
+  if (!GUARD || st + XM_NB - 1 < nst) mid_issue<(J + XM_NB - 1) % XM_NB>(P, (st + XM_NB - 1) * GC_KS);
+  __builtin_amdgcn_sched_barrier(0);
+  mid_compute<MT>(As + (st & 1) * XM_BM * GC_LDA, Bs + (st & 1) * XB_BN * GC_LDA, wm, wn, acc);
+  if (!GUARD || st + 1 < nst)
+    mid_store<(J + 1) % XM_NB, SWIGLU>(P, As + ((st + 1) & 1) * XM_BM * GC_LDA,
+                                       Bs + ((st + 1) & 1) * XB_BN * GC_LDA);
+  __syncthreads();
+}
+
+template <int J, bool GUARD, bool SWIGLU, int MT>
+__device__ __forceinline__ void mid_trip(MidPipe<MT>& P, int st, int nst, bf16_t* As, bf16_t* Bs,
+                                         f32x4 (&acc)[MT][4], int wm, int wn) {
+  mid_step<J, GUARD, SWIGLU>(P, st + J, nst, As, Bs, acc, wm, wn);
+  if constexpr (J + 1 < XM_NB) mid_trip<J + 1, GUARD, SWIGLU>(P, st, nst, As, Bs, acc, wm, wn);
+}
+
+// One medium block: rows [rb.r0, rb.r0 + rb.R) of expert rb.e, 32 (MT - 1) <
+// rb.R <= 32 MT, column block rb.nb.  L holds XM_LDS bf16.
+template <bool SWIGLU, int MT>
+__device__ __forceinline__ void mid_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
+                                          const bf16_t* __restrict__ B3, int K, int N,
+                                          bf16_t* __restrict__ C, const RowBlock& rb, int wave,
+                                          bf16_t* L) {
+  const int t = threadIdx.x;
+  const int64_t estride = (int64_t)K * N;
+  MidPipe<MT> P;
+  const bf16_t* Bp;
+  int bcol;
+  if (SWIGLU) {  // waves 0-3 load W1 blocks, waves 4-7 the same W3 blocks
+    const int u = t & 255;
+    P.kb = u >> 5;
+    P.nb = (u & 31) + (wave >= 4 ? 32 : 0);
+    Bp = (wave < 4 ? B1 : B3) + rb.e * estride;
+    bcol = rb.nb * 128 + 4 * (u & 31);
+  } else {
+    P.kb = t >> 6;
+    P.nb = t & 63;
+    Bp = B1 + rb.e * estride;
+    bcol = rb.nb * 256 + 4 * P.nb;
+  }
+  P.ra = gc_rsrc(A + (int64_t)rb.r0 * K, (uint32_t)((int64_t)rb.R * K * 2));
+  P.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
+#pragma unroll
+  for (int j = 0; j < MidPipe<MT>::AV; ++j) {
+    const int r = min((t >> 3) + 64 * j, rb.R - 1);
+    P.va[j] = (uint32_t)(((int64_t)r * K + 8 * (t & 7)) * 2);
+  }
+  P.vb = bcol < N ? (uint32_t)(((int64_t)(8 * P.kb) * N + bcol) * 2) : GC_OOR;
+  P.ldb2 = (uint32_t)(N * 2);
+  bf16_t* As = L;
+  bf16_t* Bs = L + 2 * XM_BM * GC_LDA;
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = (K + GC_KS - 1) / GC_KS;
+  mid_issue<0>(P, 0);
+  if (nst > 1) mid_issue<1>(P, GC_KS);
+  mid_store<0, SWIGLU>(P, As, Bs);
+  __syncthreads();
+  int st = 0;
+  for (; st + 2 * XM_NB - 1 <= nst; st += XM_NB)
+    mid_trip<0, false, SWIGLU>(P, st, nst, As, Bs, acc, wm, wn);
+  mid_trip<0, true, SWIGLU>(P, st, nst, As, Bs, acc, wm, wn);
+  mid_trip<0, true, SWIGLU>(P, st + XM_NB, nst, As, Bs, acc, wm, wn);
+  // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile q, rows
+  // 16 MT wm + 16 mt + 4 g + r of output column base + 4 (i or i & 7) + q
+  const int lane = t & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int ocol = SWIGLU ? rb.nb * 128 + 32 * wn + 4 * (i & 7) : rb.nb * 256 + 64 * wn + 4 * i;
+  const bool store_lane = (SWIGLU ? (i < 8) : true) && ocol < N;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = acc[mt][q][r];
+        if (SWIGLU) {
+          const float b = __shfl_xor(a, 8);
+          o[q] = a / (1.0f + expf(-a)) * b;
+        } else {
+          o[q] = a;
+        }
+      }
+      const int row = 16 * MT * wm + 16 * mt + 4 * g + r;
+      if (store_lane && row < rb.R)
+        *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * N + ocol) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+constexpr int XG_LDS = XGThin::LDS > XM_LDS ? XGThin::LDS : XM_LDS;
+static_assert(XGThin::NW == 8 && XB_NW == 8, "one workgroup size for all streamed tile classes");
+
+// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
+// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
+// Segments with fewer than `th` rows; each picks its tile class by row count.
+// K and N tails are bounded by the buffer descriptors (gemm_core.h).
+template <bool SWIGLU>
+__global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_t* __restrict__ A,
+                                                                     const int32_t* __restrict__ offsets,
+                                                                     int e_begin, int e_end,
+                                                                     const bf16_t* __restrict__ B1,
+                                                                     const bf16_t* __restrict__ B3,
+                                                                     int K, int N,
+                                                                     bf16_t* __restrict__ C, int th) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[XG_LDS];
+  __shared__ int pre[2 * (XG_MAXN + 1)];
+  // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
+  const int ncols = SWIGLU ? 2 * N : N;
+  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, pre);
+  // values from LDS and the wave index are wave-uniform; say so, so that
+  // pointers and buffer descriptors built from them live in scalar registers
+  rb.e = __builtin_amdgcn_readfirstlane(rb.e);
+  rb.r0 = __builtin_amdgcn_readfirstlane(rb.r0);
+  rb.R = __builtin_amdgcn_readfirstlane(rb.R);
+  rb.nb = __builtin_amdgcn_readfirstlane(rb.nb);
+  rb.cls = __builtin_amdgcn_readfirstlane(rb.cls);
+  if (rb.R <= 0) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (rb.cls == 0) {
+    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, wave, As);
+    return;
+  }
+  switch ((rb.R + 31) >> 5) {
+#define XM_CASE(n) \
+  case n: mid_block<SWIGLU, n>(A, B1, B3, K, N, C, rb, wave, As); break;
+    XM_CASE(1) XM_CASE(2) XM_CASE(3) XM_CASE(4) XM_CASE(5) XM_CASE(6)
+#undef XM_CASE
+    default: break;
   }
 }
 
@@ -640,12 +831,12 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // row blocks of nw blocks of weight 1; a streamed expert has fewer than
     // min(T + 1, th) rows, and the local row counts add up to at most
     // rows_max.  Each XCD's share of the blocks is at most ceil(W / 8).
-    const int64_t rbmax = (std::min<int64_t>(p.T, (int64_t)th - 1) + XGWide::BM - 1) / XGWide::BM;
+    const int64_t rbmax = (std::min<int64_t>(p.T, (int64_t)th - 1) + XM_BM - 1) / XM_BM;
     auto grid = [&](int ncols) {
       const int64_t nt = (ncols + XGThin::COLS - 1) / XGThin::COLS;
-      const int64_t nw = (ncols + XGWide::COLS - 1) / XGWide::COLS;
+      const int64_t nw = (ncols + XM_COLS - 1) / XM_COLS;
       const int64_t per_e = std::max<int64_t>(XG_WT_THIN * nt, nw);
-      const int64_t w_rows = ne * per_e + (p.rows_max * nw + XGWide::BM - 1) / XGWide::BM;
+      const int64_t w_rows = ne * per_e + (p.rows_max * nw + XM_BM - 1) / XM_BM;
       const int64_t w_exp = ne * std::max<int64_t>(XG_WT_THIN * nt, rbmax * nw);
       const int64_t w = std::min(w_rows, w_exp);
       return (unsigned)(8 * ((w + 7) / 8));
@@ -670,7 +861,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f)), dim3(64 * XGWide::NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
                        (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -681,7 +872,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, ntn);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d)), dim3(64 * XGWide::NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
                        (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th);
     return hipGetLastError();

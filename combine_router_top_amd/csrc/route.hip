@@ -327,9 +327,11 @@ static RouteKind route_kind(const Prob& p) {
 
 static int route_splits(const Prob& p) {
   if (route_kind(p) != ROUTE_WIDE) return 1;
-  // about 256 workgroups over the chip, every split keeps >= 256 of K
+  // at most one workgroup per compute unit (a second round of a few
+  // workgroups would double the time), every split keeps >= 256 of K
   const int64_t blocks = (int64_t)((p.T + RW_BM - 1) / RW_BM) * ((p.E + RW_BN - 1) / RW_BN);
-  int64_t s = (256 + blocks - 1) / blocks;
+  int64_t s = 256 / blocks;
+  if (s < 1) s = 1;
   const int64_t smax = p.d / 256 > 1 ? p.d / 256 : 1;
   if (s > smax) s = smax;
   return (int)s;
