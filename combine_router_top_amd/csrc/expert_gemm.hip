@@ -74,6 +74,14 @@ struct RowBlock {
   int e, r0, R, nb, cls;
 };
 
+// Optional A row map (GEMM-1 reading x directly instead of x_packed): packed
+// row p is row rows[p] / div of A, a matrix of `bytes` bytes.
+struct RowMap {
+  const int32_t* rows;
+  int div;
+  uint32_t bytes;
+};
+
 // Segments of at most XG_THIN_MAX rows stream through the thin tiles, larger
 // ones (below the large-tile threshold) through the wide tiles.
 #ifndef MOE_XG_THIN_MAX
@@ -169,11 +177,16 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
 template <class Cfg, bool SWIGLU, int MT>
 __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bl,
                                           int K, int N, int col, bf16_t* __restrict__ C,
-                                          const RowBlock& rb, bf16_t* As) {
+                                          const RowBlock& rb, const RowMap& rm, bf16_t* As) {
   constexpr int CPL = Cfg::CPL, NW = Cfg::NW;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
-  GemmArgs ga{A + (int64_t)rb.r0 * K, K, rb.R, Bl, N, 0, K, N, col};
+  GemmArgs ga{A + (rm.rows ? 0 : (int64_t)rb.r0 * K), K, rb.R, Bl, N, 0, K, N, col};
+  if (rm.rows) {
+    ga.rows = rm.rows + rb.r0;
+    ga.rdiv = rm.div;
+    ga.abytes = rm.bytes;
+  }
   f32x4 acc[MT][CPL];
   gemm_mainloop<NW, CPL, MT, Cfg::NB>(ga, As, acc);
 
@@ -231,8 +244,8 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
 template <class Cfg, bool SWIGLU>
 __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                              const bf16_t* __restrict__ B3, int K, int N,
-                                             bf16_t* __restrict__ C, const RowBlock& rb, int wave,
-                                             bf16_t* As) {
+                                             bf16_t* __restrict__ C, const RowBlock& rb,
+                                             const RowMap& rm, int wave, bf16_t* As) {
   const int i = threadIdx.x & 15;
   int col;
   const bf16_t* Bl;
@@ -247,7 +260,7 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
   const int mt = (rb.R + 15) >> 4;
   switch (mt) {
 #define XG_CASE(n) \
-  case n: if constexpr (n <= Cfg::MTMAX) gemm_body<Cfg, SWIGLU, n>(A, Bl, K, N, col, C, rb, As); break;
+  case n: if constexpr (n <= Cfg::MTMAX) gemm_body<Cfg, SWIGLU, n>(A, Bl, K, N, col, C, rb, rm, As); break;
     XG_CASE(1) XG_CASE(2) XG_CASE(3) XG_CASE(4) XG_CASE(5)
     XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
 #undef XG_CASE
@@ -522,8 +535,8 @@ __device__ __forceinline__ void mid_trip(MidPipe<MT>& P, int st, int nst, bf16_t
 template <bool SWIGLU, int MT>
 __device__ __forceinline__ void mid_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                           const bf16_t* __restrict__ B3, int K, int N,
-                                          bf16_t* __restrict__ C, const RowBlock& rb, int wave,
-                                          bf16_t* L) {
+                                          bf16_t* __restrict__ C, const RowBlock& rb,
+                                          const RowMap& rm, int wave, bf16_t* L) {
   const int t = threadIdx.x;
   const int64_t estride = (int64_t)K * N;
   MidPipe<MT> P;
@@ -541,12 +554,14 @@ __device__ __forceinline__ void mid_block(const bf16_t* __restrict__ A, const bf
     Bp = B1 + rb.e * estride;
     bcol = rb.nb * 256 + 4 * P.nb;
   }
-  P.ra = gc_rsrc(A + (int64_t)rb.r0 * K, (uint32_t)((int64_t)rb.R * K * 2));
+  P.ra = rm.rows ? gc_rsrc(A, rm.bytes)
+                 : gc_rsrc(A + (int64_t)rb.r0 * K, (uint32_t)((int64_t)rb.R * K * 2));
   P.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
 #pragma unroll
   for (int j = 0; j < MidPipe<MT>::AV; ++j) {
     const int r = min((t >> 3) + 64 * j, rb.R - 1);
-    P.va[j] = (uint32_t)(((int64_t)r * K + 8 * (t & 7)) * 2);
+    const int64_t row = rm.rows ? (int64_t)(rm.rows[rb.r0 + r] / rm.div) : (int64_t)r;
+    P.va[j] = (uint32_t)((row * K + 8 * (t & 7)) * 2);
   }
   P.vb = bcol < N ? (uint32_t)(((int64_t)(8 * P.kb) * N + bcol) * 2) : GC_OOR;
   P.ldb2 = (uint32_t)(N * 2);
@@ -611,7 +626,8 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
                                                                      const bf16_t* __restrict__ B1,
                                                                      const bf16_t* __restrict__ B3,
                                                                      int K, int N,
-                                                                     bf16_t* __restrict__ C, int th) {
+                                                                     bf16_t* __restrict__ C, int th,
+                                                                     RowMap rm) {
   __shared__ __attribute__((aligned(16))) bf16_t As[XG_LDS];
   __shared__ int pre[2 * (XG_MAXN + 1)];
   // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
@@ -627,12 +643,12 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   if (rb.R <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (rb.cls == 0) {
-    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, wave, As);
+    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, rm, wave, As);
     return;
   }
   switch ((rb.R + 31) >> 5) {
 #define XM_CASE(n) \
-  case n: mid_block<SWIGLU, n>(A, B1, B3, K, N, C, rb, wave, As); break;
+  case n: mid_block<SWIGLU, n>(A, B1, B3, K, N, C, rb, rm, wave, As); break;
     XM_CASE(1) XM_CASE(2) XM_CASE(3) XM_CASE(4) XM_CASE(5) XM_CASE(6)
 #undef XM_CASE
     default: break;
@@ -645,7 +661,7 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
 template <bool SWIGLU>
 __device__ __forceinline__ void big_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                          const bf16_t* __restrict__ B3, int K, int N,
-                                         bf16_t* __restrict__ C, const BigTile& bt,
+                                         bf16_t* __restrict__ C, const BigTile& bt, const RowMap& rm,
                                          bf16_t (*As)[XB_BM * GC_LDA], bf16_t (*Bs)[XB_BN * GC_LDA]) {
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -665,13 +681,14 @@ __device__ __forceinline__ void big_tile(const bf16_t* __restrict__ A, const bf1
     Bp = B1 + bt.e * estride;
     bcol = bt.nt * 256 + 4 * c.nb;
   }
-  const bf16_t* Ablk = A + (int64_t)bt.r0 * K;
-  c.ra = gc_rsrc(Ablk, (uint32_t)((int64_t)bt.R * K * 2));
+  c.ra = rm.rows ? gc_rsrc(A, rm.bytes)
+                 : gc_rsrc(A + (int64_t)bt.r0 * K, (uint32_t)((int64_t)bt.R * K * 2));
   c.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = min((t >> 3) + 64 * j, bt.R - 1);
-    c.va[j] = (uint32_t)(((int64_t)r * K + 8 * (t & 7)) * 2);
+    const int64_t row = rm.rows ? (int64_t)(rm.rows[bt.r0 + r] / rm.div) : (int64_t)r;
+    c.va[j] = (uint32_t)((row * K + 8 * (t & 7)) * 2);
   }
   c.vb = bcol < N ? (uint32_t)(((int64_t)(8 * c.kb) * N + bcol) * 2) : GC_OOR;
   c.ldb2 = (uint32_t)(N * 2);
@@ -741,7 +758,7 @@ template <bool SWIGLU>
 __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int e_begin, int e_end,
     const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3, int K, int N,
-    bf16_t* __restrict__ C, int ntn) {
+    bf16_t* __restrict__ C, int ntn, RowMap rm) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
   __shared__ int pre[XG_MAXN + 1];
@@ -767,7 +784,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     bt.r0 = __builtin_amdgcn_readfirstlane(bt.r0);
     bt.R = __builtin_amdgcn_readfirstlane(bt.R);
     bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
-    big_tile<SWIGLU>(A, B1, B3, K, N, C, bt, As, Bs);
+    big_tile<SWIGLU>(A, B1, B3, K, N, C, bt, rm, As, Bs);
   }
 }
 
@@ -818,9 +835,13 @@ size_t expert_gemm_ws_bytes(const Prob&) { return 0; }
 
 hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
                               const void* w1, const void* w3, const void* w2, void* h,
-                              void* y_packed, void*, int e_begin, int e_end, hipStream_t st) {
+                              void* y_packed, void*, int e_begin, int e_end, hipStream_t st,
+                              const int32_t* perm) {
   if (p.rows_max == 0 || e_end <= e_begin) return hipSuccess;
   if (p.dtype == 1) {
+    // with perm, x_packed is x itself and GEMM-1 reads row perm[p] / k for packed row p
+    const RowMap rm1 = perm ? RowMap{perm, p.k, (uint32_t)((int64_t)p.T * p.d * 2)} : RowMap{nullptr, 1, 0};
+    const RowMap rm2{nullptr, 1, 0};
     // experts with >= XB_TH rows go to the 256 x 256 kernel; no expert can
     // exceed T rows (top-k picks distinct experts), so small T never needs it
     const bool big = p.T >= XB_TH;
@@ -858,23 +879,23 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
       const int ntn = (p.f + 127) / 128;
       hipLaunchKernelGGL(grouped_gemm_bf16_big<true>, dim3(big_grid(ntn)), dim3(64 * XB_NW), 0, st,
                          (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                         (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn);
+                         (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn, rm1);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th);
+                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, rm1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (big) {
       const int ntn = (p.d + 255) / 256;
       hipLaunchKernelGGL(grouped_gemm_bf16_big<false>, dim3(big_grid(ntn)), dim3(64 * XB_NW), 0, st,
                          (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                         (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, ntn);
+                         (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, ntn, rm2);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th);
+                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, rm2);
     return hipGetLastError();
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);

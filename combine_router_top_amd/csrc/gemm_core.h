@@ -39,7 +39,7 @@ constexpr uint32_t GC_RSRC_W3 = 0x00020000u;  // buffer descriptor word 3 for gf
 constexpr uint32_t GC_OOR = 0x80000000u;      // lane offset that is outside every descriptor
 
 struct GemmArgs {
-  const bf16_t* A;   // first row of this block
+  const bf16_t* A;   // first row of this block (or, with rows, the row-mapped matrix)
   int64_t lda;       // A row stride (elements)
   int R;             // rows of this block (>= 1); rows past R are never stored
   const bf16_t* B;   // weight matrix [K][ldb] (row 0 = k 0)
@@ -47,7 +47,19 @@ struct GemmArgs {
   int kbeg, kend;    // K range [kbeg, kend), kbeg a multiple of 8
   int N;             // valid columns of B
   int col;           // this lane's first column (CPL consecutive)
+  // Optional row map: block row r is row rows[r] / rdiv of A, whose
+  // descriptor then spans abytes (the whole matrix).  nullptr: rows are
+  // consecutive from A.
+  const int32_t* rows = nullptr;
+  int rdiv = 1;
+  uint32_t abytes = 0;
 };
+
+// Byte offset of block row r (clamped by the caller) inside the A descriptor.
+__device__ __forceinline__ uint32_t gc_arow(const GemmArgs& g, int r) {
+  const int64_t row = g.rows ? (int64_t)(g.rows[r] / g.rdiv) : (int64_t)r;
+  return (uint32_t)(row * g.lda * 2);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gc_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -73,14 +85,15 @@ constexpr int gc_lds_elems() { return 2 * Pipe<NW, CPL, MT>::AROWS * GC_LDA; }
 
 template <int NW, int CPL, int MT, int NB>
 __device__ __forceinline__ void gc_setup(Pipe<NW, CPL, MT, NB>& P, const GemmArgs& g) {
-  // A descriptor spans the block's rows; B descriptor spans rows [0, kend).
-  P.ra = gc_rsrc(g.A, (uint32_t)((int64_t)g.R * g.lda * 2));
+  // A descriptor spans the block's rows (or the row-mapped matrix); B
+  // descriptor spans rows [0, kend).
+  P.ra = gc_rsrc(g.A, g.rows ? g.abytes : (uint32_t)((int64_t)g.R * g.lda * 2));
   P.rb = gc_rsrc(g.B, (uint32_t)((int64_t)g.kend * g.ldb * 2));
 #pragma unroll
   for (int q = 0; q < Pipe<NW, CPL, MT, NB>::AV; ++q) {
     const int v = threadIdx.x + Pipe<NW, CPL, MT, NB>::NT * q;
     const int r = min(v >> 3, g.R - 1);
-    P.va[q] = (uint32_t)(((int64_t)r * g.lda + 8 * (v & 7)) * 2);
+    P.va[q] = gc_arow(g, r) + (uint32_t)(16 * (v & 7));
   }
   const int grp = (threadIdx.x & 63) >> 4;
   P.vb = g.col < g.N ? (uint32_t)(((int64_t)(8 * grp) * g.ldb + g.col) * 2) : GC_OOR;

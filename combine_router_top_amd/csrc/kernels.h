@@ -23,11 +23,14 @@ hipError_t launch_gather(const Prob& p, const void* x, const int32_t* offsets,
                          const int32_t* perm, void* x_packed, int e_begin, int e_end,
                          hipStream_t st);
 
-// expert_gemm.hip: GEMMs over the segments of local experts [e_begin, e_end)
+// expert_gemm.hip: GEMMs over the segments of local experts [e_begin, e_end).
+// With perm (bf16 only, T * d * 2 < 2^32), x_packed is x itself and GEMM-1
+// gathers its rows through perm (packed row p = token perm[p] / k).
 size_t expert_gemm_ws_bytes(const Prob& p);
 hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
                               const void* w1, const void* w3, const void* w2, void* h,
-                              void* y_packed, void* ws, int e_begin, int e_end, hipStream_t st);
+                              void* y_packed, void* ws, int e_begin, int e_end, hipStream_t st,
+                              const int32_t* perm = nullptr);
 
 // combine.hip
 hipError_t launch_combine(const Prob& p, const void* y_packed, const int32_t* inv,

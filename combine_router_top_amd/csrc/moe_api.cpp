@@ -311,7 +311,12 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   if (e == hipSuccess)
     e = moe::launch_dispatch_index(q, idx, counts, offsets, perm, inv, ws + L.disp, s0);
   if (e != hipSuccess) return hip_status(e, "moe_layer routing");
-  if (!overlap) {
+  // bf16 with x inside one 32-bit buffer descriptor: GEMM-1 gathers the x rows
+  // itself through perm, so x_packed is never written
+  const bool fused = q.dtype == 1 && (int64_t)q.T * q.d * 2 < (int64_t(1) << 31);
+  if (!overlap && fused) {
+    e = moe::launch_expert_gemm(q, x, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0, perm);
+  } else if (!overlap) {
     e = moe::launch_gather(q, x, offsets, perm, xp, 0, q.n, s0);
     if (e == hipSuccess)
       e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0);
