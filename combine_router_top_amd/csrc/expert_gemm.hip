@@ -33,6 +33,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "gemm_core.h"
+#include "lds_tile.h"
 
 namespace moe {
 
@@ -65,8 +66,8 @@ struct XGCfg {
 using XGThin = XGCfg<8, 4, 5, 2>;
 // Medium class (more than XG_THIN_MAX rows): blocks of up to XM_BM rows and
 // XM_COLS weight columns (mid_block below).
-constexpr int XM_BM = 192;
-constexpr int XM_COLS = 256;
+constexpr int XM_BM = XT_BM;
+constexpr int XM_COLS = XT_BN;
 
 // Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb,
 // tile class (0: thin, 1: wide).
@@ -284,7 +285,7 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
 // i ^ 8.  The lower four waves load W1 blocks, the upper four W3 blocks, so
 // every buffer descriptor is wave-uniform.
 constexpr int XB_BM = 256;
-constexpr int XB_BN = 256;      // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
+constexpr int XB_BN = XT_BN;    // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
 constexpr int XB_NW = 8;        // waves per workgroup
 constexpr int XB_TH = 320;      // row count from which an expert uses this kernel
 #ifndef MOE_XB_GM
@@ -369,26 +370,6 @@ __device__ __forceinline__ void big_issue(BigRegs& R, const BigCtx& c, int k0) {
     R.b[r] = __builtin_amdgcn_raw_buffer_load_b64(c.rb, c.vb, (uint32_t)(k0 + r) * c.ldb2, 0);
 }
 
-// LDS row (within the 256-row B^T tile) of weight column c (0..3) of 4-column
-// group nb.  GEMM-1: nb 0..31 are W1 columns 4 nb .., nb 32..63 the same W3
-// columns; wave slab wn holds h columns 32 wn .. 32 wn + 31, lane i (< 8) of
-// n-tile t the h column 32 wn + 4 i + t, lane i + 8 its W3 twin.  GEMM-2: wave
-// slab wn holds weight columns 64 wn .. 64 wn + 63, lane i of n-tile t column
-// 64 wn + 4 i + t.
-template <bool SWIGLU>
-__device__ __forceinline__ int big_brow(int nb, int c) {
-  if (SWIGLU) {
-    const int m3 = nb >> 5;
-    const int hc = 4 * (nb & 31) + c;   // 0..127
-    const int wn = hc >> 5, hw = hc & 31;
-    return 64 * wn + 16 * (hw & 3) + 8 * m3 + (hw >> 2);
-  } else {
-    const int wc = 4 * nb + c;          // 0..255
-    const int wn = wc >> 6, cw = wc & 63;
-    return 64 * wn + 16 * (cw & 3) + (cw >> 2);
-  }
-}
-
 template <bool SWIGLU>
 __device__ __forceinline__ void big_store(const BigRegs& R, const BigCtx& c, bf16_t* As, bf16_t* Bs) {
   const int t = threadIdx.x;
@@ -402,7 +383,7 @@ __device__ __forceinline__ void big_store(const BigRegs& R, const BigCtx& c, bf1
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       v[q] = __builtin_amdgcn_perm(R.b[2 * q + 1][col >> 1], R.b[2 * q][col >> 1], sel);
-    *reinterpret_cast<u32x4*>(Bs + big_brow<SWIGLU>(c.nb, col) * GC_LDA + 8 * c.kb) = v;
+    *reinterpret_cast<u32x4*>(Bs + tile_brow<SWIGLU>(c.nb, col) * GC_LDA + 8 * c.kb) = v;
   }
 }
 
@@ -428,107 +409,10 @@ __device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs, 
 }
 
 // ---------------------------------------------------------------------------
-// medium segments: up to 192 rows x 256 weight columns, both operands via LDS
+// medium segments: up to 192 rows x 256 weight columns (lds_tile.h)
 // ---------------------------------------------------------------------------
-// A workgroup streams one 256-column weight block of one expert for a block of
-// up to XM_BM rows.  Each thread loads one 8 x 4 block of the 64-K weight stage
-// (32 or 64 lanes side by side along a weight row, so every load instruction
-// reads 256- or 512-byte runs of a row; 4-byte loads of 64-byte runs cap a
-// compute unit near 28 GB/s on this part) and its share of the A rows, both
-// with buffer loads, in a 3-slot register ring (two stages in flight); at the
-// end of a stage the next stage's A rows and transposed weight block are
-// written to the other LDS buffer (same B^T layout as the large tiles).  The 8
-// waves form 2 row halves x 4 column slabs: wave (wm, wn) computes rows
-// 16 MT wm .. + 16 MT - 1 against B^T rows 64 wn .. 64 wn + 63, MT = ceil(R / 32)
-// m-tiles, so each wave reads only its half of the A tile from LDS.
-constexpr int XM_NB = 3;
-constexpr int XM_LDS = 2 * (XM_BM + XB_BN) * GC_LDA;  // bf16: double-buffered A and B^T stages
-static_assert(XM_COLS == XB_BN, "medium blocks use the large-tile B^T layout");
-
-template <int MT>
-struct MidPipe {
-  static constexpr int AV = (MT + 1) / 2;   // 32 MT rows, 64 rows per 16-byte vector round
-  struct Slot {
-    u32x4 a[AV];
-    u32x2 b[8];
-  } s[XM_NB];
-  __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[AV];
-  uint32_t vb, ldb2;
-  int kb, nb;
-};
-
-template <int J, int MT>
-__device__ __forceinline__ void mid_issue(MidPipe<MT>& P, int k0) {
-#pragma unroll
-  for (int j = 0; j < MidPipe<MT>::AV; ++j)
-    P.s[J].a[j] = __builtin_amdgcn_raw_buffer_load_b128(P.ra, P.va[j], (uint32_t)(k0 * 2), 0);
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-    P.s[J].b[r] = __builtin_amdgcn_raw_buffer_load_b64(P.rb, P.vb, (uint32_t)(k0 + r) * P.ldb2, 0);
-}
-
-template <int J, bool SWIGLU, int MT>
-__device__ __forceinline__ void mid_store(const MidPipe<MT>& P, bf16_t* As, bf16_t* Bs) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < MidPipe<MT>::AV; ++j)
-    *reinterpret_cast<u32x4*>(As + ((t >> 3) + 64 * j) * GC_LDA + 8 * (t & 7)) = P.s[J].a[j];
-#pragma unroll
-  for (int col = 0; col < 4; ++col) {
-    const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      v[q] = __builtin_amdgcn_perm(P.s[J].b[2 * q + 1][col >> 1], P.s[J].b[2 * q][col >> 1], sel);
-    *reinterpret_cast<u32x4*>(Bs + big_brow<SWIGLU>(P.nb, col) * GC_LDA + 8 * P.kb) = v;
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void mid_compute(const bf16_t* As, const bf16_t* Bs, int wm, int wn,
-                                            f32x4 (&acc)[MT][4]) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, g = lane >> 4;
-  const bf16_t* a0 = As + (16 * MT * wm + i) * GC_LDA + 8 * g;
-  const bf16_t* b0 = Bs + (64 * wn + i) * GC_LDA + 8 * g;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    bf16x8 bf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      bf[t] = *reinterpret_cast<const bf16x8*>(b0 + 16 * t * GC_LDA + 32 * sub);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(a0 + 16 * mt * GC_LDA + 32 * sub);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
-    }
-  }
-}
-
-// Stage st in ring slot J = st % XM_NB: refill the slot of stage st - 1 with
-// stage st + 2, multiply stage st, write stage st + 1 into the other LDS
-// buffer, barrier.  GUARD as in gemm_core.h.
-template <int J, bool GUARD, bool SWIGLU, int MT>
-__device__ __forceinline__ void mid_step(MidPipe<MT>& P, int st, int nst, bf16_t* As, bf16_t* Bs,
-                                         f32x4 (&acc)[MT][4], int wm, int wn) {
-  if (GUARD && st >= nst) return;
-  if (!GUARD || st + XM_NB - 1 < nst) mid_issue<(J + XM_NB - 1) % XM_NB>(P, (st + XM_NB - 1) * GC_KS);
-  __builtin_amdgcn_sched_barrier(0);
-  mid_compute<MT>(As + (st & 1) * XM_BM * GC_LDA, Bs + (st & 1) * XB_BN * GC_LDA, wm, wn, acc);
-  if (!GUARD || st + 1 < nst)
-    mid_store<(J + 1) % XM_NB, SWIGLU>(P, As + ((st + 1) & 1) * XM_BM * GC_LDA,
-                                       Bs + ((st + 1) & 1) * XB_BN * GC_LDA);
-  __syncthreads();
-}
-
-template <int J, bool GUARD, bool SWIGLU, int MT>
-__device__ __forceinline__ void mid_trip(MidPipe<MT>& P, int st, int nst, bf16_t* As, bf16_t* Bs,
-                                         f32x4 (&acc)[MT][4], int wm, int wn) {
-  mid_step<J, GUARD, SWIGLU>(P, st + J, nst, As, Bs, acc, wm, wn);
-  if constexpr (J + 1 < XM_NB) mid_trip<J + 1, GUARD, SWIGLU>(P, st, nst, As, Bs, acc, wm, wn);
-}
+constexpr int XM_LDS = 2 * (XM_BM + XT_BN) * GC_LDA;  // bf16: double-buffered A and B^T stages
+static_assert(XM_COLS == XT_BN && XB_BN == XT_BN, "medium and large tiles share the B^T layout");
 
 // One medium block: rows [rb.r0, rb.r0 + rb.R) of expert rb.e, 32 (MT - 1) <
 // rb.R <= 32 MT, column block rb.nb.  L holds XM_LDS bf16.
@@ -569,20 +453,7 @@ __device__ __forceinline__ void mid_block(const bf16_t* __restrict__ A, const bf
   bf16_t* Bs = L + 2 * XM_BM * GC_LDA;
   const int wm = wave & 1, wn = wave >> 1;
   f32x4 acc[MT][4];
-#pragma unroll
-  for (int a = 0; a < MT; ++a)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nst = (K + GC_KS - 1) / GC_KS;
-  mid_issue<0>(P, 0);
-  if (nst > 1) mid_issue<1>(P, GC_KS);
-  mid_store<0, SWIGLU>(P, As, Bs);
-  __syncthreads();
-  int st = 0;
-  for (; st + 2 * XM_NB - 1 <= nst; st += XM_NB)
-    mid_trip<0, false, SWIGLU>(P, st, nst, As, Bs, acc, wm, wn);
-  mid_trip<0, true, SWIGLU>(P, st, nst, As, Bs, acc, wm, wn);
-  mid_trip<0, true, SWIGLU>(P, st + XM_NB, nst, As, Bs, acc, wm, wn);
+  mid_mainloop<SWIGLU, MT>(P, 0, K, As, Bs, acc, wm, wn);
   // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile q, rows
   // 16 MT wm + 16 mt + 4 g + r of output column base + 4 (i or i & 7) + q
   const int lane = t & 63;
