@@ -131,6 +131,14 @@ __device__ __forceinline__ void mid_trip(MidPipe<MT>& P, int st, int nst, bf16_t
 }
 
 
+template <int J, int MT>
+__device__ __forceinline__ void mid_prologue(MidPipe<MT>& P, int kbeg, int nst) {
+  if constexpr (J < XT_NB - 1) {
+    if (J < nst) mid_issue<J>(P, kbeg + J * GC_KS);
+    mid_prologue<J + 1>(P, kbeg, nst);
+  }
+}
+
 // The K loop over [kbeg, kend) (kbeg a multiple of 8; rows of B past the B
 // descriptor read zero).  P holds the descriptors and lane offsets; As/Bs
 // point at XT_BM / XT_BN double buffers of GC_LDA-strided rows.
@@ -144,8 +152,7 @@ __device__ __forceinline__ void mid_mainloop(MidPipe<MT>& P, int kbeg, int kend,
   const int nst = (kend - kbeg + GC_KS - 1) / GC_KS;
   if (nst <= 0) return;
   P.kbeg = kbeg;
-  mid_issue<0>(P, kbeg);
-  if (nst > 1) mid_issue<1>(P, kbeg + GC_KS);
+  mid_prologue<0>(P, kbeg, nst);  // stages 0 .. XT_NB - 2 into slots 0 .. XT_NB - 2
   mid_store<0, SWIGLU>(P, As, Bs);
   __syncthreads();
   int st = 0;
