@@ -25,6 +25,7 @@ namespace moe {
 
 constexpr int DCH = 1024;   // assignments per chunk
 constexpr int DMAXE = 1024; // max experts
+constexpr int DUN = 16;     // chunk histograms read per round in the scatter prologue
 
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ idx,
                                                          int64_t TK, int E,
@@ -78,9 +79,21 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int c = blockIdx.x;
 
   // 1. per local expert: total count and count in the chunks before this one
+  // (DUN independent loads in flight per round instead of one round trip per chunk)
   for (int e = tid; e < n; e += 256) {
     int tot = 0, pre = 0;
-    for (int cc = 0; cc < nchunks; ++cc) {
+    int cc = 0;
+    for (; cc + DUN <= nchunks; cc += DUN) {
+      int v[DUN];
+#pragma unroll
+      for (int u = 0; u < DUN; ++u) v[u] = chunk_hist[(int64_t)(cc + u) * E + lo + e];
+#pragma unroll
+      for (int u = 0; u < DUN; ++u) {
+        pre += cc + u < c ? v[u] : 0;
+        tot += v[u];
+      }
+    }
+    for (; cc < nchunks; ++cc) {
       const int v = chunk_hist[(int64_t)cc * E + lo + e];
       pre += cc < c ? v : 0;
       tot += v;
@@ -113,7 +126,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     if (tid == 0) offsets[n] = total;
     for (int e = tid; e < E; e += 256) {
       int t = 0;
-      for (int cc = 0; cc < nchunks; ++cc) t += chunk_hist[(int64_t)cc * E + e];
+      int cc = 0;
+      for (; cc + DUN <= nchunks; cc += DUN) {
+        int v[DUN];
+#pragma unroll
+        for (int u = 0; u < DUN; ++u) v[u] = chunk_hist[(int64_t)(cc + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < DUN; ++u) t += v[u];
+      }
+      for (; cc < nchunks; ++cc) t += chunk_hist[(int64_t)cc * E + e];
       counts_all[e] = t;
     }
   }
