@@ -7,22 +7,25 @@
 //   GEMM-2:  y_packed[R] = rnd(h[R] W2_e)
 //
 // bf16 path (grouped_gemm_bf16).  A workgroup owns one row block of one
-// expert (up to 160 or 80 rows, see XGCfg) and one column block; every weight byte of that
+// expert and one 512-column block of its weights; every weight byte of that
 // column block is streamed from HBM exactly once per row block, which is the
 // bound for the segment sizes of a sparse MoE layer (about 4..160 rows per
-// expert).  8 waves (2 per SIMD) share the A rows through LDS; each wave
-// streams its own weight columns (2 or 4 per lane) straight from HBM into
-// registers and transposes them there into MFMA B fragments (mfma_tile.h,
-// gemm_core.h).  The row-block schedule is derived on the
-// device from `offsets` in the workgroup prologue, so the number of local
-// assignments never travels to the host; the grid is sized for the worst case
-// and surplus workgroups exit after the prologue.
-//
-// GEMM-1 pairs W1 and W3: the lower half of the waves streams W1 columns and
-// the upper half the same W3 columns (each wave reads one weight matrix, so its
-// buffer descriptor is wave-uniform); after the K loop the upper half passes
-// its products to the lower half through LDS, which applies SiLU(x.W1)*(x.W3)
-// and writes h.  The intermediate products never reach memory.
+// expert).  Two tile classes share the kernel:
+//   thin (segments of at most XG_THIN_MAX rows, decode): 8 waves (2 per SIMD)
+//     share the A rows through LDS; each wave streams its own weight columns
+//     (4 per lane) straight from HBM into registers and transposes them there
+//     into MFMA B fragments (mfma_tile.h, gemm_core.h).  GEMM-1 pairs W1 and
+//     W3: the lower half of the waves streams W1 columns and the upper half
+//     the same W3 columns; after the K loop the upper half passes its products
+//     to the lower half through LDS, which applies SiLU(x.W1)*(x.W3).
+//   medium (up to XM_BM rows per block, prefill): both operands are copied
+//     from memory straight into a 3-slot LDS ring and multiplied with the
+//     weights as the MFMA row operand (dma_tile.h); W1 and W3 products of an
+//     h column meet in one register.
+// The row-block schedule is derived on the device from `offsets` in the
+// workgroup prologue, so the number of local assignments never travels to the
+// host; the grid is sized for the worst case and surplus workgroups exit
+// after the prologue.  The intermediate products never reach memory.
 //
 // fp32 path (grouped_gemm_f32): one thread per output element, for the small
 // fp32 problems only.
@@ -34,17 +37,15 @@
 #include "kernels.h"
 #include "gemm_core.h"
 #include "lds_tile.h"
+#include "dma_tile.h"
 
 namespace moe {
 
 constexpr int XG_MAXN = 1024;             // max local experts
 
-// Tile configurations of the streaming kernel.  "Wide" suits segments of
-// ~100-160 rows (prefill): 160-row blocks, 2 weight columns per lane; "thin"
-// suits segments of a few rows (decode), where the kernel is a pure weight
-// stream and wider (8-byte) weight loads keep the load-instruction rate
-// down: 80-row blocks, 4 columns per lane.  The host picks one from the
-// expected rows per expert.
+// Register-streamed tile configuration (the thin class): segments of a few
+// rows (decode), where the kernel is a pure weight stream and 8-byte weight
+// loads keep the load-instruction rate down: 80-row blocks, 4 columns per lane.
 template <int NW_, int CPL_, int MTMAX_, int NB_>
 struct XGCfg {
   static constexpr int NB = NB_;                 // register ring depth
@@ -65,12 +66,12 @@ struct XGCfg {
 };
 using XGThin = XGCfg<8, 4, 5, 2>;
 // Medium class (more than XG_THIN_MAX rows): blocks of up to XM_BM rows and
-// XM_COLS weight columns (mid_block below).
-constexpr int XM_BM = XT_BM;
-constexpr int XM_COLS = XT_BN;
+// XM_COLS weight columns (dt_block, dma_tile.h).
+constexpr int XM_BM = DT_BM;
+constexpr int XM_COLS = DT_BN;
 
 // Row block of this workgroup: expert e, rows [r0, r0 + R), column block nb,
-// tile class (0: thin, 1: wide).
+// tile class (0: thin, 1: medium).
 struct RowBlock {
   int e, r0, R, nb, cls;
 };
@@ -84,14 +85,14 @@ struct RowMap {
 };
 
 // Segments of at most XG_THIN_MAX rows stream through the thin tiles, larger
-// ones (below the large-tile threshold) through the wide tiles.
+// ones (below the large-tile threshold) through the medium tiles.
 #ifndef MOE_XG_THIN_MAX
 #define MOE_XG_THIN_MAX 48
 #endif
 constexpr int XG_THIN_MAX = MOE_XG_THIN_MAX;
 
 static_assert(XG_THIN_MAX <= XGThin::BM, "a thin segment is one row block");
-// Work of a block in units of a wide block: the path is bound by the weight
+// Work of a block in units of a medium block: the path is bound by the weight
 // stream, which grows with the block's column count.
 constexpr int XG_WT_THIN = XGThin::COLS / XM_COLS;
 static_assert(XG_WT_THIN * XM_COLS == XGThin::COLS, "thin columns a multiple of medium ones");
@@ -106,8 +107,8 @@ __device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls) {
 // Schedule from `offsets` (computed by every workgroup, a few hundred cycles).
 // Experts in [e_begin, e_end) with fewer than `th` rows contribute (row block,
 // column block) pairs of their tile class.  The blocks are listed thin class
-// first, then wide, each by ascending expert; a thin block weighs XG_WT_THIN,
-// a wide one 1, and block i starts at the running sum of the weights before
+// first, then medium, each by ascending expert; a thin block weighs XG_WT_THIN,
+// a medium one 1, and block i starts at the running sum of the weights before
 // it.  XCD x (workgroup id mod 8 on this part) takes the blocks that start in
 // [ceil(x W / 8), ceil((x + 1) W / 8)) of the total work W, the q-th of them
 // going to its q-th workgroup.  Every XCD thus gets an equal share of the
@@ -178,7 +179,8 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
 template <class Cfg, bool SWIGLU, int MT>
 __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bl,
                                           int K, int N, int col, bf16_t* __restrict__ C,
-                                          const RowBlock& rb, const RowMap& rm, bf16_t* As) {
+                                          const RowBlock& rb, const RowMap& rm, bf16_t* As,
+                                          float* xch0, float* xch1) {
   constexpr int CPL = Cfg::CPL, NW = Cfg::NW;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -192,13 +194,13 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
   gemm_mainloop<NW, CPL, MT, Cfg::NB>(ga, As, acc);
 
   // GEMM-1: waves of the upper half hold the x.W3 products of the columns the
-  // lower half holds x.W1 for; they hand them over through LDS.
+  // lower half holds x.W1 for; they hand them over through LDS (pairs
+  // 0 .. NW/4 - 1 through xch0, the others through xch1).
   bool store_wave = true;
-  float* xch = reinterpret_cast<float*>(As);
   if (SWIGLU) {
     store_wave = wave < NW / 2;
     const int pair = wave % (NW / 2);
-    float* slot = xch + pair * (Cfg::MTMAX * CPL * 4 * 64) + lane;
+    float* slot = (pair < NW / 4 ? xch0 : xch1) + (pair % (NW / 4)) * (Cfg::MTMAX * CPL * 4 * 64) + lane;
     if (!store_wave) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -246,7 +248,8 @@ template <class Cfg, bool SWIGLU>
 __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                              const bf16_t* __restrict__ B3, int K, int N,
                                              bf16_t* __restrict__ C, const RowBlock& rb,
-                                             const RowMap& rm, int wave, bf16_t* As) {
+                                             const RowMap& rm, int wave, bf16_t* As, float* xch0,
+                                             float* xch1) {
   const int i = threadIdx.x & 15;
   int col;
   const bf16_t* Bl;
@@ -261,7 +264,7 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
   const int mt = (rb.R + 15) >> 4;
   switch (mt) {
 #define XG_CASE(n) \
-  case n: if constexpr (n <= Cfg::MTMAX) gemm_body<Cfg, SWIGLU, n>(A, Bl, K, N, col, C, rb, rm, As); break;
+  case n: if constexpr (n <= Cfg::MTMAX) gemm_body<Cfg, SWIGLU, n>(A, Bl, K, N, col, C, rb, rm, As, xch0, xch1); break;
     XG_CASE(1) XG_CASE(2) XG_CASE(3) XG_CASE(4) XG_CASE(5)
     XG_CASE(6) XG_CASE(7) XG_CASE(8) XG_CASE(9) XG_CASE(10)
 #undef XG_CASE
@@ -408,83 +411,12 @@ __device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs, 
   }
 }
 
-// ---------------------------------------------------------------------------
-// medium segments: up to 192 rows x 256 weight columns (lds_tile.h)
-// ---------------------------------------------------------------------------
-constexpr int XM_LDS = 2 * (XM_BM + XT_BN) * GC_LDA;  // bf16: double-buffered A and B^T stages
-static_assert(XM_COLS == XT_BN && XB_BN == XT_BN, "medium and large tiles share the B^T layout");
-
-// One medium block: rows [rb.r0, rb.r0 + rb.R) of expert rb.e, 32 (MT - 1) <
-// rb.R <= 32 MT, column block rb.nb.  L holds XM_LDS bf16.
-template <bool SWIGLU, int MT>
-__device__ __forceinline__ void mid_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
-                                          const bf16_t* __restrict__ B3, int K, int N,
-                                          bf16_t* __restrict__ C, const RowBlock& rb,
-                                          const RowMap& rm, int wave, bf16_t* L) {
-  const int t = threadIdx.x;
-  const int64_t estride = (int64_t)K * N;
-  MidPipe<MT> P;
-  const bf16_t* Bp;
-  int bcol;
-  if (SWIGLU) {  // waves 0-3 load W1 blocks, waves 4-7 the same W3 blocks
-    const int u = t & 255;
-    P.kb = u >> 5;
-    P.nb = (u & 31) + (wave >= 4 ? 32 : 0);
-    Bp = (wave < 4 ? B1 : B3) + rb.e * estride;
-    bcol = rb.nb * 128 + 4 * (u & 31);
-  } else {
-    P.kb = t >> 6;
-    P.nb = t & 63;
-    Bp = B1 + rb.e * estride;
-    bcol = rb.nb * 256 + 4 * P.nb;
-  }
-  P.ra = rm.rows ? gc_rsrc(A, rm.bytes)
-                 : gc_rsrc(A + (int64_t)rb.r0 * K, (uint32_t)((int64_t)rb.R * K * 2));
-  P.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
-#pragma unroll
-  for (int j = 0; j < MidPipe<MT>::AV; ++j) {
-    const int r = min((t >> 3) + 64 * j, rb.R - 1);
-    const int64_t row = rm.rows ? (int64_t)(rm.rows[rb.r0 + r] / rm.div) : (int64_t)r;
-    P.va[j] = (uint32_t)((row * K + 8 * (t & 7)) * 2);
-  }
-  P.vb = bcol < N ? (uint32_t)(((int64_t)(8 * P.kb) * N + bcol) * 2) : GC_OOR;
-  P.ldb2 = (uint32_t)(N * 2);
-  bf16_t* As = L;
-  bf16_t* Bs = L + 2 * XM_BM * GC_LDA;
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[MT][4];
-  mid_mainloop<SWIGLU, MT>(P, 0, K, As, Bs, acc, wm, wn);
-  // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile q, rows
-  // 16 MT wm + 16 mt + 4 g + r of output column base + 4 (i or i & 7) + q
-  const int lane = t & 63;
-  const int i = lane & 15, g = lane >> 4;
-  const int ocol = SWIGLU ? rb.nb * 128 + 32 * wn + 4 * (i & 7) : rb.nb * 256 + 64 * wn + 4 * i;
-  const bool store_lane = (SWIGLU ? (i < 8) : true) && ocol < N;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = acc[mt][q][r];
-        if (SWIGLU) {
-          const float b = __shfl_xor(a, 8);
-          o[q] = a / (1.0f + expf(-a)) * b;
-        } else {
-          o[q] = a;
-        }
-      }
-      const int row = 16 * MT * wm + 16 * mt + 4 * g + r;
-      if (store_lane && row < rb.R)
-        *reinterpret_cast<u32x2*>(C + (int64_t)(rb.r0 + row) * N + ocol) =
-            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
-  }
-}
-
-constexpr int XG_LDS = XGThin::LDS > XM_LDS ? XGThin::LDS : XM_LDS;
 static_assert(XGThin::NW == 8 && XB_NW == 8, "one workgroup size for all streamed tile classes");
+// The thin tiles borrow the medium ring slots: the A stages in slot 0, the
+// W3 -> W1 accumulator exchange in slots 1 and 2 (half of the pairs each).
+static_assert(2 * gc_lds_elems<XGThin::NW, XGThin::CPL, XGThin::MTMAX>() <= DT_SLOT,
+              "thin A stages fit one slot");
+static_assert(XGThin::XCH / 2 * 4 <= DT_SLOT, "half of the thin exchange fits one slot");
 
 // SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
@@ -499,7 +431,10 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
                                                                      int K, int N,
                                                                      bf16_t* __restrict__ C, int th,
                                                                      RowMap rm) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[XG_LDS];
+  __shared__ __attribute__((aligned(16))) char S0[DT_SLOT];
+  __shared__ __attribute__((aligned(16))) char S1[DT_SLOT];
+  __shared__ __attribute__((aligned(16))) char S2[DT_SLOT];
+  __shared__ uint32_t dtab[DT_AI * 512];
   __shared__ int pre[2 * (XG_MAXN + 1)];
   // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
   const int ncols = SWIGLU ? 2 * N : N;
@@ -514,13 +449,18 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   if (rb.R <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (rb.cls == 0) {
-    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, rm, wave, As);
+    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, rm, wave, reinterpret_cast<bf16_t*>(S0),
+                                 reinterpret_cast<float*>(S1), reinterpret_cast<float*>(S2));
     return;
   }
+  const DtSlots slots{{S0, S1, S2}, dtab};
   switch ((rb.R + 31) >> 5) {
-#define XM_CASE(n) \
-  case n: mid_block<SWIGLU, n>(A, B1, B3, K, N, C, rb, rm, wave, As); break;
-    XM_CASE(1) XM_CASE(2) XM_CASE(3) XM_CASE(4) XM_CASE(5) XM_CASE(6)
+#define XM_CASE(n)                                                                              \
+  case n:                                                                                       \
+    dt_block<SWIGLU, n>(A, B1, B3, K, N, C, rb.e, rb.r0, rb.R, rb.nb, rm.rows, rm.div, rm.bytes, \
+                        wave, slots);                                                           \
+    break;
+    XM_CASE(1) XM_CASE(2) XM_CASE(3) XM_CASE(4) XM_CASE(5)
 #undef XM_CASE
     default: break;
   }
@@ -719,7 +659,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     const int th = big ? XB_TH : INT32_MAX;
     const int ne = e_end - e_begin;
     // Streaming grid: the total work W of schedule().  A thin expert is one
-    // row block of nt blocks of weight XG_WT_THIN, a wide one ceil(cnt / BM)
+    // row block of nt blocks of weight XG_WT_THIN, a medium one ceil(cnt / BM)
     // row blocks of nw blocks of weight 1; a streamed expert has fewer than
     // min(T + 1, th) rows, and the local row counts add up to at most
     // rows_max.  Each XCD's share of the blocks is at most ceil(W / 8).
