@@ -10,8 +10,7 @@
 // pipe of a compute unit near its streaming rate).  Three LDS slots form a
 // ring: two stages are in flight while the third is multiplied.  A stage is
 // released by an explicit wait for the wave's own copies (vmcnt) and one
-// barrier; the slots are distinct LDS objects so that the compiler's own
-// waits before LDS reads only cover copies into the slot being read.
+// barrier.
 //
 // The MFMA runs with the weights as its 16-row operand: a lane's fragment, 8
 // consecutive k of one weight column, comes from two ds_read_b64_tr_b16 reads
@@ -172,7 +171,10 @@ __device__ __forceinline__ void dt_compute(const DtCtx<MT>& c, const DtSlots& S,
 }
 
 // Stage st in slot J = st % 3: wait for it, refill the slot of stage st - 1
-// with stage st + 2, multiply.  GUARD: the form with range conditions (tail).
+// (every wave is past it) with stage st + 2, multiply.  GUARD: the form with
+// range conditions (tail).  (Refilling a slot right after its own multiply,
+// behind a second barrier, keeps three stages in flight but puts the multiply
+// on the critical path; it measured slower.)
 template <int J, bool GUARD, bool SWIGLU, int MT>
 __device__ __forceinline__ void dt_step(const DtCtx<MT>& c, const DtSlots& S, int st, int nst, int K,
                                         f32x4 (&acc)[MT][8]) {
@@ -191,15 +193,16 @@ __device__ __forceinline__ void dt_trip(const DtCtx<MT>& c, const DtSlots& S, in
 }
 
 // One medium block: rows [r0, r0 + R) of expert e (32 (MT - 1) < R <= 32 MT,
-// R >= 1), weight column block nb (GEMM-1: h columns 256 nb .., GEMM-2:
-// output columns 512 nb ..).  A row r is A[r0 + r] or, with a row map, row
+// R >= 1), weight column block nb of mcols columns (a multiple of 64, at most
+// DT_BN; GEMM-1: h columns mcols / 2 * nb .. + mcols / 2 - 1 of W1 and W3,
+// GEMM-2: output columns mcols * nb .. + mcols - 1).  A row r is A[r0 + r] or, with a row map, row
 // rows[r0 + r] / rdiv of the abytes-byte matrix A.  K and N multiples of 8.
 //   SWIGLU: C[r0 + r][h] = rnd(SiLU(A W1) * (A W3)),  B1/B3 = [E][K][N]
 //   else:   C[r0 + r][n] = rnd(A W2),                   B1 = [E][K][N]
 template <bool SWIGLU, int MT>
 __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                          const bf16_t* __restrict__ B3, int K, int N,
-                                         bf16_t* __restrict__ C, int e, int r0, int R, int nb,
+                                         bf16_t* __restrict__ C, int e, int r0, int R, int nb, int mcols,
                                          const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
                                          int wave, const DtSlots& S) {
   const int lane = threadIdx.x & 63;
@@ -211,7 +214,9 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
   // panel rows 8 (w & 3) .. + 7, two rows per instruction
   const int panel = wave >> 2;
   const bf16_t* Bp = (SWIGLU && panel ? B3 : B1) + e * estride;
-  const int colbase = SWIGLU ? 256 * nb : 512 * nb + 256 * panel;
+  const int cblk = SWIGLU ? (mcols >> 1) * nb : mcols * nb;       // first column of the block
+  const int cend = min(N, cblk + (SWIGLU ? mcols >> 1 : mcols));  // columns past it are not used
+  const int colbase = SWIGLU ? cblk : cblk + 256 * panel;
   c.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
   c.ldb2 = (uint32_t)(N * 2);
   // rows j and j + 4 of a copy pair share dt_swb (it depends on j & 3 and j & 8)
@@ -219,7 +224,7 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
   for (int u = 0; u < 2; ++u) {
     const int j = 8 * (wave & 3) + 2 * u + (lane >> 5);
     const int col = colbase + 8 * ((lane & 31) ^ dt_swb(j));
-    c.vb[u] = col < N ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
+    c.vb[u] = col < cend ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
   }
   c.bdst = panel * DT_PANEL + 4096 * (wave & 3);
   // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row.
@@ -268,14 +273,14 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
     const int row = 16 * MT * wm + 16 * mt + i;
 #pragma unroll
     for (int t = 0; t < (SWIGLU ? 4 : 8); ++t) {
-      const int col = SWIGLU ? 256 * nb + 64 * wn + 16 * t + 4 * g : 512 * nb + 128 * wn + 16 * t + 4 * g;
+      const int col = cblk + (SWIGLU ? 64 * wn : 128 * wn) + 16 * t + 4 * g;
       float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acc[mt][t][r];
         o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a;
       }
-      if (row < R && col < N)
+      if (row < R && col < cend)
         *reinterpret_cast<u32x2*>(C + (int64_t)(r0 + row) * N + col) =
             u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }

@@ -92,32 +92,36 @@ struct RowMap {
 constexpr int XG_THIN_MAX = MOE_XG_THIN_MAX;
 
 static_assert(XG_THIN_MAX <= XGThin::BM, "a thin segment is one row block");
-// Work of a block in units of a medium block: the path is bound by the weight
-// stream, which grows with the block's column count.
-constexpr int XG_WT_THIN = XGThin::COLS / XM_COLS;
-static_assert(XG_WT_THIN * XM_COLS == XGThin::COLS, "thin columns a multiple of medium ones");
+// Work of a block in units of 64 weight columns: the path is bound by the
+// weight stream, which grows with the block's column count.  Medium blocks
+// span mcols weight columns (a multiple of 64, at most XM_COLS), chosen per
+// launch by the host.
+constexpr int XG_WUNIT = 64;
+constexpr int XG_WT_THIN = XGThin::COLS / XG_WUNIT;
+static_assert(XG_WT_THIN * XG_WUNIT == XGThin::COLS, "thin columns a multiple of the work unit");
 
 // Blocks of class `cls` of one expert with `cnt` rows (0 for the other class).
-__device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls) {
+__device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls, int mcols) {
   if (cnt <= 0 || cnt >= th || (cnt <= XG_THIN_MAX ? 0 : 1) != cls) return 0;
   if (cls == 0) return (ncols + XGThin::COLS - 1) / XGThin::COLS;
-  return (cnt + XM_BM - 1) / XM_BM * ((ncols + XM_COLS - 1) / XM_COLS);
+  return (cnt + XM_BM - 1) / XM_BM * ((ncols + mcols - 1) / mcols);
 }
 
 // Schedule from `offsets` (computed by every workgroup, a few hundred cycles).
 // Experts in [e_begin, e_end) with fewer than `th` rows contribute (row block,
 // column block) pairs of their tile class.  The blocks are listed thin class
 // first, then medium, each by ascending expert; a thin block weighs XG_WT_THIN,
-// a medium one 1, and block i starts at the running sum of the weights before
-// it.  XCD x (workgroup id mod 8 on this part) takes the blocks that start in
+// a medium one mcols / XG_WUNIT, and block i starts at the running sum of the
+// weights before it.  XCD x (workgroup id mod 8 on this part) takes the blocks that start in
 // [ceil(x W / 8), ceil((x + 1) W / 8)) of the total work W, the q-th of them
 // going to its q-th workgroup.  Every XCD thus gets an equal share of the
 // weight stream, the column blocks of one row block mostly share one L2 for
-// their A rows, and within an XCD the longer thin blocks start first.  The
-// grid needs 8 ceil(W / 8) workgroups at most.  R = 0 means "exit".
+// their A rows, and within an XCD the longer thin blocks start first.  Block
+// starts are at least the smaller weight apart, so the grid needs
+// 8 ceil(ceil(W / 8) / min weight) workgroups at most.  R = 0 means "exit".
 // `pre` holds 2 (XG_MAXN + 1) ints.
 __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, int e_end,
-                             int th, int ncols, int* pre) {
+                             int th, int ncols, int mcols, int* pre) {
   const int ne = e_end - e_begin;
   int* prew = pre + XG_MAXN + 1;
   if (threadIdx.x < 64) {
@@ -126,8 +130,8 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
     for (int j0 = 0; j0 < ne; j0 += 64) {
       const int j = j0 + lane;
       const int cnt = j < ne ? offsets[e_begin + j + 1] - offsets[e_begin + j] : 0;
-      int xt = xg_blocks(cnt, th, ncols, 0);
-      int xw = xg_blocks(cnt, th, ncols, 1);
+      int xt = xg_blocks(cnt, th, ncols, 0, mcols);
+      int xw = xg_blocks(cnt, th, ncols, 1, mcols);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int yt = __shfl_up(xt, off);
@@ -143,15 +147,16 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   __syncthreads();
   RowBlock rb{0, 0, 0, 0, 0};
   const int nth = pre[XG_MAXN], nwd = prew[XG_MAXN];
+  const int wm = mcols / XG_WUNIT;                   // work of a medium block
   const int wth = XG_WT_THIN * nth;                  // work of the thin blocks
-  const int W = wth + nwd;
+  const int W = wth + wm * nwd;
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int w0 = (xcd * W + 7) >> 3, w1 = ((xcd + 1) * W + 7) >> 3;
   // first block starting at or after w0, then this workgroup's block
-  const int i0 = w0 <= wth ? (w0 + XG_WT_THIN - 1) / XG_WT_THIN : nth + (w0 - wth);
+  const int i0 = w0 <= wth ? (w0 + XG_WT_THIN - 1) / XG_WT_THIN : nth + (w0 - wth + wm - 1) / wm;
   const int i = i0 + q;
   if (i >= nth + nwd) return rb;
-  const int start = i < nth ? XG_WT_THIN * i : wth + (i - nth);
+  const int start = i < nth ? XG_WT_THIN * i : wth + wm * (i - nth);
   if (start >= w1) return rb;
   rb.cls = i < nth ? 0 : 1;
   const int* P = rb.cls ? prew : pre;
@@ -166,7 +171,7 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   const int o = offsets[e];
   const int cnt = offsets[e + 1] - o;
   const int bm = rb.cls ? XM_BM : XGThin::BM;
-  const int cols = rb.cls ? XM_COLS : XGThin::COLS;
+  const int cols = rb.cls ? mcols : XGThin::COLS;
   const int nblk = (ncols + cols - 1) / cols;
   const int jb = local / nblk;
   rb.nb = local - jb * nblk;
@@ -295,6 +300,10 @@ constexpr int XB_TH = 320;      // row count from which an expert uses this kern
 #define MOE_XB_GM 8
 #endif
 constexpr int XB_GM = MOE_XB_GM; // m-tiles grouped together along the XCD-local order
+// Large-tile workgroups per compute unit when few or no segments reach XB_TH.
+#ifndef MOE_XB_SPARSE_WG
+#define MOE_XB_SPARSE_WG 4
+#endif
 
 struct BigTile {
   int e, r0, R, nt;
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
                                                                      const bf16_t* __restrict__ B3,
                                                                      int K, int N,
                                                                      bf16_t* __restrict__ C, int th,
-                                                                     RowMap rm) {
+                                                                     int mcols, RowMap rm) {
   __shared__ __attribute__((aligned(16))) char S0[DT_SLOT];
   __shared__ __attribute__((aligned(16))) char S1[DT_SLOT];
   __shared__ __attribute__((aligned(16))) char S2[DT_SLOT];
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   __shared__ int pre[2 * (XG_MAXN + 1)];
   // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
   const int ncols = SWIGLU ? 2 * N : N;
-  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, pre);
+  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, mcols, pre);
   // values from LDS and the wave index are wave-uniform; say so, so that
   // pointers and buffer descriptors built from them live in scalar registers
   rb.e = __builtin_amdgcn_readfirstlane(rb.e);
@@ -457,8 +466,8 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   switch ((rb.R + 31) >> 5) {
 #define XM_CASE(n)                                                                              \
   case n:                                                                                       \
-    dt_block<SWIGLU, n>(A, B1, B3, K, N, C, rb.e, rb.r0, rb.R, rb.nb, rm.rows, rm.div, rm.bytes, \
-                        wave, slots);                                                           \
+    dt_block<SWIGLU, n>(A, B1, B3, K, N, C, rb.e, rb.r0, rb.R, rb.nb, mcols, rm.rows, rm.div,    \
+                        rm.bytes, wave, slots);                                                 \
     break;
     XM_CASE(1) XM_CASE(2) XM_CASE(3) XM_CASE(4) XM_CASE(5)
 #undef XM_CASE
@@ -658,21 +667,43 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     const bool big = p.T >= XB_TH;
     const int th = big ? XB_TH : INT32_MAX;
     const int ne = e_end - e_begin;
-    // Streaming grid: the total work W of schedule().  A thin expert is one
-    // row block of nt blocks of weight XG_WT_THIN, a medium one ceil(cnt / BM)
-    // row blocks of nw blocks of weight 1; a streamed expert has fewer than
-    // min(T + 1, th) rows, and the local row counts add up to at most
-    // rows_max.  Each XCD's share of the blocks is at most ceil(W / 8).
-    const int64_t rbmax = (std::min<int64_t>(p.T, (int64_t)th - 1) + XM_BM - 1) / XM_BM;
-    auto grid = [&](int ncols) {
-      const int64_t nt = (ncols + XGThin::COLS - 1) / XGThin::COLS;
-      const int64_t nw = (ncols + XM_COLS - 1) / XM_COLS;
-      const int64_t per_e = std::max<int64_t>(XG_WT_THIN * nt, nw);
-      const int64_t w_rows = ne * per_e + (p.rows_max * nw + XM_BM - 1) / XM_BM;
-      const int64_t w_exp = ne * std::max<int64_t>(XG_WT_THIN * nt, rbmax * nw);
-      const int64_t w = std::min(w_rows, w_exp);
-      return (unsigned)(8 * ((w + 7) / 8));
+    // Medium column blocks: when the expected segment is a single medium row
+    // block, pick the width (512, 448 or 384 weight columns) whose block count
+    // fills the last round of workgroups best (one workgroup per compute
+    // unit); e.g. 7168 output columns x 32 experts: 448 gives exactly 2 rounds
+    // where 512 gives 1.75.
+    const int cus = big_cus();
+    const int64_t mean_rows = (int64_t)p.T * p.k / std::max(1, p.E);
+    auto pick_mcols = [&](int ncols) {
+      if (mean_rows <= XG_THIN_MAX || mean_rows > XM_BM) return XM_COLS;
+      int best = XM_COLS;
+      double best_fill = 0.0;
+      for (int cw = XM_COLS; cw >= 384; cw -= 64) {
+        const int64_t nb = (int64_t)ne * ((ncols + cw - 1) / cw);
+        const double fill = (double)nb / (double)(((nb + cus - 1) / cus) * cus);
+        if (fill > best_fill + 1e-9) { best_fill = fill; best = cw; }
+      }
+      return best;
     };
+    // Streaming grid: the total work W of schedule() (units of XG_WUNIT
+    // columns).  A thin expert is one row block of nt blocks of weight
+    // XG_WT_THIN, a medium one ceil(cnt / BM) row blocks of nw blocks of
+    // weight wm; a streamed expert has fewer than min(T + 1, th) rows, and the
+    // local row counts add up to at most rows_max.  Each XCD's blocks start in
+    // a window of ceil(W / 8) at least min(XG_WT_THIN, wm) apart.
+    const int64_t rbmax = (std::min<int64_t>(p.T, (int64_t)th - 1) + XM_BM - 1) / XM_BM;
+    auto grid = [&](int ncols, int mcols) {
+      const int64_t wm = mcols / XG_WUNIT;
+      const int64_t nt = (ncols + XGThin::COLS - 1) / XGThin::COLS;
+      const int64_t nw = (ncols + mcols - 1) / mcols;
+      const int64_t per_e = std::max<int64_t>(XG_WT_THIN * nt, wm * nw);
+      const int64_t w_rows = ne * per_e + wm * ((p.rows_max * nw + XM_BM - 1) / XM_BM);
+      const int64_t w_exp = ne * std::max<int64_t>(XG_WT_THIN * nt, wm * rbmax * nw);
+      const int64_t w = std::min(w_rows, w_exp);
+      const int64_t wmin = std::min<int64_t>(XG_WT_THIN, wm);
+      return (unsigned)(8 * ((((w + 7) / 8) + wmin - 1) / wmin));
+    };
+    const int mc1 = pick_mcols(2 * p.f), mc2 = pick_mcols(p.d);
     // Large-tile grid.  Its tiles: sum over experts with n_e >= XB_TH of
     // ceil(n_e / BM) <= rows_max / BM + min(ne, rows_max / XB_TH) m-tiles, times
     // ntn.  When the mean segment reaches XB_TH rows (dense-like routing) the
@@ -683,7 +714,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     const bool dense_like = (int64_t)p.T * p.k >= (int64_t)XB_TH * p.E;
     auto big_grid = [&](int ntn) {
       const int64_t w = bblocks * ntn;
-      return (unsigned)(dense_like ? w : std::min<int64_t>(w, 4 * (int64_t)big_cus()));
+      return (unsigned)(dense_like ? w : std::min<int64_t>(w, MOE_XB_SPARSE_WG * (int64_t)big_cus()));
     };
     hipError_t e;
     if (big) {
@@ -693,9 +724,9 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn, rm1);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f)), dim3(64 * XGThin::NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f, mc1)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, rm1);
+                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, mc1, rm1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (big) {
       const int ntn = (p.d + 255) / 256;
@@ -704,9 +735,9 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, ntn, rm2);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d)), dim3(64 * XGThin::NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d, mc2)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, rm2);
+                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, mc2, rm2);
     return hipGetLastError();
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);

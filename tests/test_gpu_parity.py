@@ -33,8 +33,15 @@ SMALL = {
     "big_tails": W("big_tails", 1500, 328, 4, 2, 264, 0, 4, "bf16", seed=14),
     # skewed: some experts on the large-tile kernel, the rest streamed
     "big_mixed": W("big_mixed", 1200, 256, 16, 4, 256, 0, 8, "bf16", skew=True, seed=15),
-    # all three tile classes (thin <= 48 rows, wide, large >= 320) with column tails
+    # all three tile classes (thin <= 48 rows, medium, large >= 320) with column tails
     "mixed_classes": W("mixed_classes", 700, 264, 24, 4, 328, 0, 12, "bf16", skew=True, seed=16),
+    # ~60 rows per expert on 16 local experts: the host narrows the medium
+    # column blocks so that they fill the last round of workgroups (GEMM-2:
+    # 7168 columns in 448-column blocks; GEMM-1: 2 x 3072 weight columns in
+    # 384-column blocks), thin and medium blocks mixed under the
+    # column-weighted XCD split
+    "narrow_mcols_down": W("narrow_mcols_down", 480, 7168, 16, 2, 128, 0, 16, "bf16", seed=17),
+    "narrow_mcols_up": W("narrow_mcols_up", 480, 128, 16, 2, 3072, 0, 16, "bf16", seed=18),
 }
 
 _cache = {}
@@ -121,7 +128,8 @@ def test_dispatch_supplied_indices(pattern):
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_combine_identity_experts(name):
     """y_packed := x_packed gives y = rnd(x * sum of local weights); with all
-    experts local the bf16 output equals x bit for bit."""
+    experts local the bf16 output equals x in value (a -0.0 in x comes back as
+    +0.0: the weighted sum starts from +0)."""
     w, inp, ref, d = case(name)
     p = M.Spec.of(w)
     idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
@@ -133,7 +141,7 @@ def test_combine_identity_experts(name):
     none = ~(inv >= 0).any(1)
     assert np.all(O.widen(y, w.dtype)[none] == 0)
     if w.n_local == w.E and w.dtype == "bf16":
-        assert np.array_equal(y, inp["x"])
+        assert np.array_equal(O.widen(y, w.dtype), O.widen(inp["x"], w.dtype))
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
