@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy that measures practical HBM bandwidth")
+    ap.add_argument("--ab-padded", nargs="*", metavar="WORKLOAD",
+                    help="A/B of the padded fixed-capacity dispatch against the unpadded "
+                         "segments on the given workloads (default: the two skewed ones); "
+                         "prints one JSON object per workload instead of the bench line")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "then WRITE_SIZE, --output-format csv) into "
@@ -199,10 +203,104 @@ def cpu_baseline(w, inp, budget):
             "seconds": dt, "tokens": Ts}
 
 
+def ab_padded(a):
+    """Padded fixed-capacity dispatch vs the unpadded segments: per workload,
+    the same routing goes through dispatch -> expert GEMM -> combine once
+    unpadded and once per capacity C (largest local count: no drops; 1.25x and
+    2x the mean count: drops; T: the static no-drop bound), each call timed
+    with HIP events on the launch stream (a.steps iterations after 2 warm-up
+    iterations)."""
+    import numpy as np
+    import torch
+
+    import combine_router_top_amd as M
+    import workloads
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    names = a.ab_padded or ["dsv3_decode_skew", "dsv3_prefill_skew"]
+    for wl in names:
+        w = workloads.get(wl)
+        inp = workloads.generate(w)
+
+        def dev(x):
+            if x is None:
+                return None
+            x = np.ascontiguousarray(x)
+            if x.dtype == np.uint16:
+                return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(x).cuda()
+        d = {k: dev(v) for k, v in inp.items()}
+        p = M.Spec.of(w)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+        torch.cuda.synchronize()
+        unp = M.dispatch(p, idx, d["x"])
+        torch.cuda.synchronize()
+        counts = np.diff(unp["offsets"].cpu().numpy())
+        A = int(counts.sum())
+        mean = w.T * w.k / w.E
+        caps = [("max_count", max(1, int(counts.max()))), ("1.25x_mean", int(np.ceil(1.25 * mean))),
+                ("2x_mean", int(np.ceil(2 * mean))), ("T", w.T)]
+        y = torch.empty((w.T, w.d), dtype=dt, device="cuda")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+        def timed(run3):
+            tot = [0.0, 0.0, 0.0]
+            for it in range(a.steps + 2):
+                ev[0].record(stream)
+                run3[0]()
+                ev[1].record(stream)
+                run3[1]()
+                ev[2].record(stream)
+                run3[2]()
+                ev[3].record(stream)
+                torch.cuda.synchronize()
+                if it >= 2:
+                    for j in range(3):
+                        tot[j] += ev[j].elapsed_time(ev[j + 1])
+            return [t / a.steps * 1e3 for t in tot]
+
+        rows = w.rows_max
+        h = torch.empty((rows, w.f), dtype=dt, device="cuda")
+        yp = torch.empty((rows, w.d), dtype=dt, device="cuda")
+        ws_d = M.alloc_workspace(p, M.MOE_CALL_DISPATCH)
+        us = timed([lambda: M.dispatch(p, idx, d["x"], workspace=ws_d, out=unp),
+                    lambda: M.expert_gemm(p, unp["x_packed"], unp["offsets"], d["w1"], d["w3"],
+                                          d["w2"], out=(h, yp)),
+                    lambda: M.combine(p, yp, unp["inv"], wt, out=y)])
+        res = {"workload": wl, "A_local": A, "counts_max": int(counts.max()),
+               "counts_min": int(counts.min()), "mean_count": mean,
+               "unpadded": {"rows": A, "dispatch_us": us[0], "gemm_us": us[1], "combine_us": us[2]}}
+        del h, yp
+        for label, C in caps:
+            prow = w.n_local * C
+            ws_p = M.alloc_workspace(p, M.MOE_CALL_DISPATCH_PADDED)
+            o = M.dispatch_padded(p, C, idx, d["x"], workspace=ws_p)
+            h = torch.empty((prow, w.f), dtype=dt, device="cuda")
+            yp = torch.empty((prow, w.d), dtype=dt, device="cuda")
+            us = timed([lambda: M.dispatch_padded(p, C, idx, d["x"], workspace=ws_p, out=o),
+                        lambda: M.expert_gemm_padded(p, C, o["x_packed"], o["offsets"], d["w1"],
+                                                     d["w3"], d["w2"], out=(h, yp)),
+                        lambda: M.combine(p, yp, o["inv"], wt, out=y, rows=prow)])
+            kept = int((o["inv"] >= 0).sum().item())
+            res[label] = {"capacity": C, "rows": prow, "dropped_frac": 1.0 - kept / max(1, A),
+                          "dispatch_us": us[0], "gemm_us": us[1], "combine_us": us[2],
+                          "gemm_vs_unpadded": us[1] / res["unpadded"]["gemm_us"]}
+            del o, h, yp, ws_p
+            torch.cuda.empty_cache()
+        print(json.dumps(res), flush=True)
+        del d
+        torch.cuda.empty_cache()
+
+
 def main():
     a = parse()
     if a.write_traffic:
         write_traffic(a)
+        return
+    if a.ab_padded is not None:
+        ab_padded(a)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:

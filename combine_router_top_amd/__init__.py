@@ -12,6 +12,8 @@ Functions (same names as the C calls):
     expert_gemm(p, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
     combine(p, y_packed, inv, topk_w) -> y
     layer(p, x, w_gate, bias, w1, w3, w2, routing=False, overlap=False, ...) -> y or (y, dict)
+    dispatch_padded(p, capacity, topk_idx, x) -> dict(counts_all, offsets, perm, inv, x_packed)
+    expert_gemm_padded(p, capacity, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
 """
 from __future__ import annotations
 
@@ -27,9 +29,11 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_F_WRITE_LOGITS, MOE_F_OVERLAP = 1, 2
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_EXPERT_GEMM, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
+MOE_CALL_DISPATCH_PADDED, MOE_CALL_EXPERT_GEMM_PADDED = 5, 6
 
 EXPORTED = ["moe_last_error", "moe_version", "moe_workspace_bytes", "moe_route", "moe_dispatch",
-            "moe_expert_gemm", "moe_combine", "moe_layer"]
+            "moe_expert_gemm", "moe_combine", "moe_layer", "moe_dispatch_padded",
+            "moe_expert_gemm_padded"]
 
 
 class MoeError(RuntimeError):
@@ -71,7 +75,10 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
         L.moe_layer.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(RoutingOut), vp, sz,
                                 vp, vp]
-        for n in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_layer"):
+        L.moe_dispatch_padded.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_gemm_padded.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for n in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_layer",
+                  "moe_dispatch_padded", "moe_expert_gemm_padded"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -232,10 +239,12 @@ def expert_gemm(p: Spec, x_packed, offsets, w1, w3, w2, workspace=None, stream=N
     return h, yp
 
 
-def combine(p: Spec, y_packed, inv, topk_w, stream=None, out=None):
+def combine(p: Spec, y_packed, inv, topk_w, stream=None, out=None, rows: Optional[int] = None):
+    """``rows``: rows of y_packed (default rows_max; n_local * capacity for
+    the padded layout)."""
     torch = _torch()
     dt = _dt(p)
-    _need(y_packed, (p.rows_max, p.d), dt, "y_packed")
+    _need(y_packed, (p.rows_max if rows is None else rows, p.d), dt, "y_packed")
     _need(inv, (p.T * p.k,), torch.int32, "inv")
     _need(topk_w, (p.T, p.k), torch.float32, "topk_w")
     y = torch.empty((p.T, p.d), dtype=dt, device=y_packed.device) if out is None else out
@@ -243,6 +252,63 @@ def combine(p: Spec, y_packed, inv, topk_w, stream=None, out=None):
     _check(lib().moe_combine(ctypes.byref(pc), _ptr(y_packed), _ptr(inv), _ptr(topk_w), _ptr(y),
                              _stream(stream)))
     return y
+
+
+def dispatch_padded(p: Spec, capacity: int, topk_idx, x, workspace=None, stream=None,
+                    out=None) -> Dict[str, object]:
+    """Padded fixed-capacity dispatch: n_local * capacity rows.  Fresh
+    outputs are pre-filled (perm with -7, x_packed with ones) so that
+    rows the call fails to write are visible."""
+    torch = _torch()
+    dt = _dt(p)
+    _need(topk_idx, (p.T, p.k), torch.int32, "topk_idx")
+    _need(x, (p.T, p.d), dt, "x")
+    rows = p.n_local * int(capacity)
+    dev = x.device
+    o = out if out is not None else {
+        "counts_all": torch.empty(p.E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(p.n_local + 1, dtype=torch.int32, device=dev),
+        "perm": torch.full((rows,), -7, dtype=torch.int32, device=dev),
+        "inv": torch.empty(p.T * p.k, dtype=torch.int32, device=dev),
+        "x_packed": torch.ones((rows, p.d), dtype=dt, device=dev),
+    }
+    _need(o["counts_all"], (p.E,), torch.int32, "counts_all")
+    _need(o["offsets"], (p.n_local + 1,), torch.int32, "offsets")
+    _need(o["perm"], (rows,), torch.int32, "perm")
+    _need(o["inv"], (p.T * p.k,), torch.int32, "inv")
+    _need(o["x_packed"], (rows, p.d), dt, "x_packed")
+    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_DISPATCH_PADDED, dev)
+    pc = p.c()
+    _check(lib().moe_dispatch_padded(ctypes.byref(pc), int(capacity), _ptr(topk_idx), _ptr(x),
+                                     _ptr(o["counts_all"]), _ptr(o["offsets"]), _ptr(o["perm"]),
+                                     _ptr(o["inv"]), _ptr(o["x_packed"]), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)))
+    return o
+
+
+def expert_gemm_padded(p: Spec, capacity: int, x_packed, offsets, w1, w3, w2, workspace=None,
+                       stream=None, out=None):
+    torch = _torch()
+    dt = _dt(p)
+    rows = p.n_local * int(capacity)
+    _need(x_packed, (rows, p.d), dt, "x_packed")
+    _need(offsets, (p.n_local + 1,), torch.int32, "offsets")
+    _need(w1, (p.n_local, p.d, p.f), dt, "w1")
+    _need(w3, (p.n_local, p.d, p.f), dt, "w3")
+    _need(w2, (p.n_local, p.f, p.d), dt, "w2")
+    dev = x_packed.device
+    if out is None:
+        h = torch.ones((rows, p.f), dtype=dt, device=dev)
+        yp = torch.ones((rows, p.d), dtype=dt, device=dev)
+    else:
+        h, yp = out
+    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_EXPERT_GEMM_PADDED, dev)
+    pc = p.c()
+    _check(lib().moe_expert_gemm_padded(ctypes.byref(pc), int(capacity), _ptr(x_packed),
+                                        _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(h),
+                                        _ptr(yp), _ptr(ws), 0 if ws is None else ws.numel(),
+                                        _stream(stream)))
+    return h, yp
 
 
 def layer(p: Spec, x, w_gate, bias, w1, w3, w2, routing: bool = False, want_logits: bool = False,

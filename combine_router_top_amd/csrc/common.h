@@ -11,7 +11,8 @@ struct Prob {
   int T, d, E, k, f, lo, n;  // n = n_local
   int dtype;                 // 0 = f32, 1 = bf16
   uint32_t flags;
-  int64_t rows_max;          // T * min(k, n)
+  int64_t rows_max;          // T * min(k, n); n * capacity for the padded layout
+  int64_t seg_rows = 0;      // rows of every local segment when fixed (padded layout), else 0
   int64_t tk() const { return (int64_t)T * k; }
   int elem() const { return dtype == 1 ? 2 : 4; }
 };

@@ -18,6 +18,8 @@
 //                      prefix in LDS, and inside a wave the rank among equal
 //                      experts from ballots over the expert-id bits.
 //   gather_rows_kernel one wave per packed row, 16-byte vector copies.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -225,6 +227,68 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Padded fixed-capacity layout (an A/B against the unpadded segments): local
+// expert e owns rows [e C, (e + 1) C); its first min(count_e, C) local
+// assignments in ascending a fill them in order, later ones are dropped, and
+// the remaining rows are padding (perm -1, zero rows).  Derived from the
+// unpadded dispatch: rank r of an assignment inside its expert is its packed
+// position minus offsets[e].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ perm_u,
+                                                       const int32_t* __restrict__ offsets_u, int n,
+                                                       int C, int32_t* __restrict__ perm,
+                                                       int32_t* __restrict__ offsets) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q <= n) offsets[q] = (int32_t)(q * C);
+  if (q >= (int64_t)n * C) return;
+  const int e = (int)(q / C), r = (int)(q - (int64_t)e * C);
+  const int o = offsets_u[e], cnt = offsets_u[e + 1] - o;
+  perm[q] = r < cnt ? perm_u[o + r] : -1;
+}
+
+__global__ __launch_bounds__(256) void pad_inv_kernel(const int32_t* __restrict__ idx, int64_t TK,
+                                                      const int32_t* __restrict__ offsets_u, int lo,
+                                                      int C, int32_t* __restrict__ inv) {
+  const int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a >= TK) return;
+  const int pos = inv[a];
+  if (pos < 0) return;
+  const int e = idx[a] - lo;
+  const int r = pos - offsets_u[e];
+  inv[a] = r < C ? e * C + r : -1;
+}
+
+// x_packed[q] = x[perm[q] / k], or a zero row where perm[q] < 0; one wave per row.
+__global__ __launch_bounds__(256) void gather_padded_kernel(const u32x4* __restrict__ x,
+                                                            const int32_t* __restrict__ perm,
+                                                            u32x4* __restrict__ xp, int nvec, int k,
+                                                            int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (q >= rows) return;
+  const int a = perm[q];
+  u32x4* dst = xp + q * nvec;
+  if (a < 0) {
+    for (int v = lane; v < nvec; v += 64) dst[v] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const u32x4* src = x + (int64_t)(a / k) * nvec;
+  for (int v0 = lane; v0 < nvec; v0 += 256) {
+    u32x4 buf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + 64 * u;
+      if (v < nvec) buf[u] = src[v];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + 64 * u;
+      if (v < nvec) dst[v] = buf[u];
+    }
+  }
+}
+
 static int64_t n_chunks(const Prob& p) { return (p.tk() + DCH - 1) / DCH; }
 
 size_t dispatch_ws_bytes(const Prob& p) { return (size_t)n_chunks(p) * p.E * sizeof(int32_t); }
@@ -252,6 +316,35 @@ hipError_t launch_gather(const Prob& p, const void* x, const int32_t* offsets,
   dim3 grid((unsigned)((rows + 3) / 4));
   hipLaunchKernelGGL(gather_rows_kernel, grid, dim3(256), 0, st, (const u32x4*)x, offsets, perm,
                      (u32x4*)x_packed, nvec, p.k, e_begin, e_end);
+  return hipGetLastError();
+}
+
+size_t dispatch_padded_ws_bytes(const Prob& p) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  return up(dispatch_ws_bytes(p)) + up((size_t)(p.n + 1) * 4) + up((size_t)p.rows_max * 4);
+}
+
+hipError_t launch_dispatch_padded(const Prob& p, int capacity, const int32_t* idx,
+                                  int32_t* counts_all, int32_t* offsets, int32_t* perm,
+                                  int32_t* inv, const void* x, void* x_packed, void* ws,
+                                  hipStream_t st) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  char* w = reinterpret_cast<char*>(ws);
+  int32_t* offsets_u = reinterpret_cast<int32_t*>(w + up(dispatch_ws_bytes(p)));
+  int32_t* perm_u = reinterpret_cast<int32_t*>(w + up(dispatch_ws_bytes(p)) + up((size_t)(p.n + 1) * 4));
+  hipError_t e = launch_dispatch_index(p, idx, counts_all, offsets_u, perm_u, inv, ws, st);
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.n * capacity;
+  const int64_t tq = std::max<int64_t>(rows, p.n + 1);
+  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((tq + 255) / 256)), dim3(256), 0, st, perm_u,
+                     offsets_u, p.n, capacity, perm, offsets);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(pad_inv_kernel, dim3((unsigned)((p.tk() + 255) / 256)), dim3(256), 0, st, idx,
+                     p.tk(), offsets_u, p.lo, capacity, inv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int nvec = (int)((int64_t)p.d * p.elem() / 16);
+  hipLaunchKernelGGL(gather_padded_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     (const u32x4*)x, perm, (u32x4*)x_packed, nvec, p.k, rows);
   return hipGetLastError();
 }
 

@@ -673,7 +673,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // unit); e.g. 7168 output columns x 32 experts: 448 gives exactly 2 rounds
     // where 512 gives 1.75.
     const int cus = big_cus();
-    const int64_t mean_rows = (int64_t)p.T * p.k / std::max(1, p.E);
+    const int64_t mean_rows = p.seg_rows ? p.seg_rows : (int64_t)p.T * p.k / std::max(1, p.E);
     auto pick_mcols = [&](int ncols) {
       if (mean_rows <= XG_THIN_MAX || mean_rows > XM_BM) return XM_COLS;
       int best = XM_COLS;
@@ -711,7 +711,7 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // or no large segments and at most 4 workgroups per compute unit loop over
     // them, which keeps an empty launch short.
     const int64_t bblocks = (p.rows_max + XB_BM - 1) / XB_BM + std::min<int64_t>(ne, p.rows_max / XB_TH);
-    const bool dense_like = (int64_t)p.T * p.k >= (int64_t)XB_TH * p.E;
+    const bool dense_like = p.seg_rows ? p.seg_rows >= XB_TH : (int64_t)p.T * p.k >= (int64_t)XB_TH * p.E;
     auto big_grid = [&](int ntn) {
       const int64_t w = bblocks * ntn;
       return (unsigned)(dense_like ? w : std::min<int64_t>(w, MOE_XB_SPARSE_WG * (int64_t)big_cus()));

@@ -23,6 +23,14 @@ hipError_t launch_gather(const Prob& p, const void* x, const int32_t* offsets,
                          const int32_t* perm, void* x_packed, int e_begin, int e_end,
                          hipStream_t st);
 
+// Padded fixed-capacity layout: n * capacity rows (see dispatch.hip); the
+// workspace holds the unpadded index plus the dispatch workspace.
+size_t dispatch_padded_ws_bytes(const Prob& p);
+hipError_t launch_dispatch_padded(const Prob& p, int capacity, const int32_t* idx,
+                                  int32_t* counts_all, int32_t* offsets, int32_t* perm,
+                                  int32_t* inv, const void* x, void* x_packed, void* ws,
+                                  hipStream_t st);
+
 // expert_gemm.hip: GEMMs over the segments of local experts [e_begin, e_end).
 // With perm (bf16 only, T * d * 2 < 2^32), x_packed is x itself and GEMM-1
 // gathers its rows through perm (packed row p = token perm[p] / k).

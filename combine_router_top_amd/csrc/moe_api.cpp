@@ -117,6 +117,8 @@ size_t call_ws_bytes(const moe::Prob& p, int32_t call) {
     case MOE_CALL_EXPERT_GEMM: return moe::expert_gemm_ws_bytes(p);
     case MOE_CALL_COMBINE: return 0;
     case MOE_CALL_LAYER: return layer_ws(p).total;
+    case MOE_CALL_DISPATCH_PADDED: return moe::dispatch_padded_ws_bytes(p);
+    case MOE_CALL_EXPERT_GEMM_PADDED: return moe::expert_gemm_ws_bytes(p);
     default: return 0;
   }
 }
@@ -129,6 +131,18 @@ moe_status_t check_ws(const moe::Prob& p, int32_t call, const void* ws, size_t b
     return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, need);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return MOE_OK;
+}
+
+// Capacity of the padded layout: 1 <= capacity <= T (no expert receives more
+// than T assignments), and the padded buffers stay addressable.
+moe_status_t check_capacity(const moe::Prob& q, int32_t capacity) {
+  if (capacity <= 0 || capacity > q.T)
+    return fail(MOE_ERR_INVALID_ARG, "capacity=%d outside [1, T=%d]", capacity, q.T);
+  const int64_t rows = (int64_t)q.n * capacity;
+  const int64_t wide = (int64_t)(q.d > q.f ? q.d : q.f) * q.elem();
+  if (rows >= ((int64_t)1 << 31) || rows * wide >= ((int64_t)1 << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "n_local*capacity=%lld rows too large", (long long)rows);
   return MOE_OK;
 }
 
@@ -168,7 +182,7 @@ const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
 size_t moe_workspace_bytes(const moe_problem_t* p, int32_t call) {
   moe::Prob q;
   if (check_problem(p, &q) != MOE_OK) return 0;
-  if (call < MOE_CALL_ROUTE || call > MOE_CALL_LAYER) {
+  if (call < MOE_CALL_ROUTE || call > MOE_CALL_EXPERT_GEMM_PADDED) {
     fail(MOE_ERR_INVALID_ARG, "unknown call %d", call);
     return 0;
   }
@@ -243,6 +257,60 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const
   return hip_status(moe::launch_expert_gemm(q, x_packed, offsets, w1, w3, w2, h, y_packed, workspace,
                                             0, q.n, (hipStream_t)stream),
                     "moe_expert_gemm");
+}
+
+moe_status_t moe_dispatch_padded(const moe_problem_t* p, int32_t capacity, const int32_t* topk_idx,
+                                 const void* x, int32_t* counts_all, int32_t* offsets, int32_t* perm,
+                                 int32_t* inv, void* x_packed, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  if ((st = check_capacity(q, capacity)) != MOE_OK) return st;
+  NEED_PTR(topk_idx);
+  NEED_PTR(x);
+  NEED_PTR(counts_all);
+  NEED_PTR(offsets);
+  NEED_PTR(perm);
+  NEED_PTR(inv);
+  NEED_PTR(x_packed);
+  NEED_ALIGNED(x);
+  NEED_ALIGNED(x_packed);
+  if ((st = check_ws(q, MOE_CALL_DISPATCH_PADDED, workspace, workspace_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(moe::launch_dispatch_padded(q, capacity, topk_idx, counts_all, offsets, perm, inv,
+                                                x, x_packed, workspace, (hipStream_t)stream),
+                    "moe_dispatch_padded");
+}
+
+moe_status_t moe_expert_gemm_padded(const moe_problem_t* p, int32_t capacity, const void* x_packed,
+                                    const int32_t* offsets, const void* w1, const void* w3,
+                                    const void* w2, void* h, void* y_packed, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  if ((st = check_capacity(q, capacity)) != MOE_OK) return st;
+  NEED_PTR(x_packed);
+  NEED_PTR(offsets);
+  NEED_PTR(w1);
+  NEED_PTR(w3);
+  NEED_PTR(w2);
+  NEED_PTR(h);
+  NEED_PTR(y_packed);
+  NEED_ALIGNED(x_packed);
+  NEED_ALIGNED(w1);
+  NEED_ALIGNED(w3);
+  NEED_ALIGNED(w2);
+  NEED_ALIGNED(h);
+  NEED_ALIGNED(y_packed);
+  if ((st = check_ws(q, MOE_CALL_EXPERT_GEMM_PADDED, workspace, workspace_bytes)) != MOE_OK) return st;
+  q.rows_max = (int64_t)q.n * capacity;
+  q.seg_rows = capacity;
+  (void)hipGetLastError();
+  return hip_status(moe::launch_expert_gemm(q, x_packed, offsets, w1, w3, w2, h, y_packed, workspace,
+                                            0, q.n, (hipStream_t)stream),
+                    "moe_expert_gemm_padded");
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int32_t* inv,

@@ -15,6 +15,8 @@
  *   moe_expert_gemm  SwiGLU expert FFNs as grouped GEMMs over the segments
  *   moe_combine      weighted un-permute and sum back to token order
  *   moe_layer        all of the above, stream-ordered
+ *   moe_dispatch_padded, moe_expert_gemm_padded
+ *                    the padded fixed-capacity layout, as an A/B
  *
  * The pages state no formulas; the definitions below are the plain MoE layer
  * (softmax top-k gating renormalised over the selected k, ties to the lower
@@ -73,7 +75,9 @@ enum {
   MOE_CALL_DISPATCH = 1,
   MOE_CALL_EXPERT_GEMM = 2,
   MOE_CALL_COMBINE = 3,
-  MOE_CALL_LAYER = 4
+  MOE_CALL_LAYER = 4,
+  MOE_CALL_DISPATCH_PADDED = 5,
+  MOE_CALL_EXPERT_GEMM_PADDED = 6
 };
 
 /*
@@ -176,6 +180,7 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const
 
 /*
  * Combine (CUCo, Table 4, "MoE Dispatch/Combine"): un-permute and weighted sum,
+ * over the unpadded or the padded layout (y_packed rows are read at inv),
  *   y[t] = rnd(sum over j < k with inv[t*k+j] >= 0 of topk_w[t,j] * y_packed[inv[t*k+j]])
  * accumulated in fp32 in slot order.  A token with no local slot gets an exact
  * zero row; every row of y is written.
@@ -183,6 +188,40 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const
  */
 moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int32_t* inv,
                          const float* topk_w, void* y, void* stream);
+
+/*
+ * Padded fixed-capacity dispatch: the layout with per-expert padding that CUCo
+ * (Table 4, row "MoE Dispatch/Combine") names as a bottleneck on imbalanced
+ * ranks, provided as an A/B against moe_dispatch's unpadded segments.  Local
+ * expert e owns rows [e*capacity, (e+1)*capacity) of x_packed.  Its first
+ * min(count_e, capacity) local assignments in ascending a fill them in that
+ * order; later ones are dropped (inv = -1, so moe_combine leaves them out) and
+ * the rows past count_e are padding.
+ *   capacity   rows per local expert, 1 .. T
+ *   counts_all [E]                  as moe_dispatch (before any drop)
+ *   offsets    [n_local+1]          offsets[e] = e * capacity
+ *   perm       [n_local*capacity]   perm[q] = a, or -1 for a padding row
+ *   inv        [T*k]                inv[a] = q for kept local assignments, else -1
+ *   x_packed   [n_local*capacity,d] x_packed[q] = x[perm[q] / k]; padding rows zero
+ *   workspace of moe_workspace_bytes(p, MOE_CALL_DISPATCH_PADDED) bytes
+ */
+moe_status_t moe_dispatch_padded(const moe_problem_t* p, int32_t capacity, const int32_t* topk_idx,
+                                 const void* x, int32_t* counts_all, int32_t* offsets, int32_t* perm,
+                                 int32_t* inv, void* x_packed, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * moe_expert_gemm over the padded layout of moe_dispatch_padded: every local
+ * expert's segment is its capacity rows (padding rows included, which give
+ * zero rows of h and y_packed).  Same arguments as moe_expert_gemm with
+ * x_packed, h and y_packed of n_local*capacity rows and offsets[e] = e*capacity;
+ * workspace of moe_workspace_bytes(p, MOE_CALL_EXPERT_GEMM_PADDED) bytes.
+ * moe_combine works on the padded y_packed unchanged (it reads rows inv[a]).
+ */
+moe_status_t moe_expert_gemm_padded(const moe_problem_t* p, int32_t capacity, const void* x_packed,
+                                    const int32_t* offsets, const void* w1, const void* w3,
+                                    const void* w2, void* h, void* y_packed, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * The whole layer: moe_route, moe_dispatch, moe_expert_gemm, moe_combine in

@@ -49,11 +49,14 @@ __all__ = [
     "topk_softmax",
     "expert_counts",
     "local_dispatch",
+    "local_dispatch_padded",
     "gather_rows",
+    "gather_rows_padded",
     "silu",
     "swiglu_experts",
     "combine",
     "moe_layer",
+    "moe_layer_padded",
     "token_outputs",
 ]
 
@@ -178,6 +181,46 @@ def gather_rows(x: np.ndarray, perm: np.ndarray, k: int) -> np.ndarray:
     return np.asarray(x)[np.asarray(perm, dtype=np.int64) // k]
 
 
+def local_dispatch_padded(topk_idx: np.ndarray, E: int, expert_lo: int, n_local: int,
+                          capacity: int):
+    """Padded fixed-capacity layout: the per-expert padded buffers that CUCo
+    (Table 4, "MoE Dispatch/Combine") names as a bottleneck on imbalanced
+    ranks.  Local expert e owns rows [e*C, (e+1)*C).  Walking the assignments
+    a = t*k + j in ascending order, a local assignment takes the next free row
+    of its expert while one is left; later ones are dropped.  Rows left over
+    are padding.
+
+    Returns (counts_all int32[E], offsets int32[n_local+1] = e*C,
+    perm int32[n_local*C] with -1 for padding, inv int32[T*k] with -1 for
+    non-local and dropped assignments).
+    """
+    flat = np.asarray(topk_idx).ravel().astype(np.int64)
+    counts_all = expert_counts(flat, E)
+    C = int(capacity)
+    perm = np.full(n_local * C, -1, dtype=np.int32)
+    inv = np.full(flat.shape[0], -1, dtype=np.int32)
+    used = [0] * n_local
+    for a in range(flat.shape[0]):
+        e = int(flat[a]) - expert_lo
+        if 0 <= e < n_local and used[e] < C:
+            q = e * C + used[e]
+            perm[q] = a
+            inv[a] = q
+            used[e] += 1
+    offsets = (np.arange(n_local + 1, dtype=np.int64) * C).astype(np.int32)
+    return counts_all, offsets, perm, inv
+
+
+def gather_rows_padded(x: np.ndarray, perm: np.ndarray, k: int) -> np.ndarray:
+    """x_packed[q] = x[perm[q] // k]; a padding row (perm -1) is all-zero bits."""
+    x = np.asarray(x)
+    perm = np.asarray(perm, dtype=np.int64)
+    out = np.zeros((perm.shape[0],) + x.shape[1:], dtype=x.dtype)
+    keep = perm >= 0
+    out[keep] = x[perm[keep] // k]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # 6-7. SwiGLU experts
 # ---------------------------------------------------------------------------
@@ -256,6 +299,28 @@ def moe_layer(p, inputs: Dict[str, np.ndarray], routing: Optional[Dict[str, np.n
         h, yp = swiglu_experts(xp, offsets, inputs["w1"], inputs["w3"], inputs["w2"], p.dtype)
         out["h"], out["y_packed"] = h, yp
         out["y"] = combine(yp, inv, w, p.dtype)
+    return out
+
+
+def moe_layer_padded(p, inputs: Dict[str, np.ndarray], capacity: int,
+                     routing: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+    """The layer over the padded fixed-capacity layout: as ``moe_layer`` with
+    step 5-6 replaced by ``local_dispatch_padded`` / ``gather_rows_padded``
+    (dropped assignments contribute nothing to y; padding rows run through
+    the experts as zero rows)."""
+    out: Dict[str, np.ndarray] = {}
+    L = router_logits(inputs["x"], inputs["w_gate"], p.dtype, inputs.get("bias"))
+    idx, w = topk_softmax(L, p.k)
+    if routing is not None:
+        idx, w = routing["topk_idx"], routing["topk_w"]
+    out["topk_idx"], out["topk_w"] = idx, w
+    counts_all, offsets, perm, inv = local_dispatch_padded(idx, p.E, p.expert_lo, p.n_local, capacity)
+    out.update(counts_all=counts_all, offsets=offsets, perm=perm, inv=inv)
+    xp = gather_rows_padded(inputs["x"], perm, p.k)
+    out["x_packed"] = xp
+    h, yp = swiglu_experts(xp, offsets, inputs["w1"], inputs["w3"], inputs["w2"], p.dtype)
+    out["h"], out["y_packed"] = h, yp
+    out["y"] = combine(yp, inv, w, p.dtype)
     return out
 
 

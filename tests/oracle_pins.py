@@ -197,6 +197,70 @@ def pin_dispatch_brute_force(O):
         assert perm.dtype == np.int32 and inv.dtype == np.int32 and offsets.dtype == np.int32
 
 
+def pin_dispatch_padded_reduces_to_unpadded(O):
+    """With a capacity of at least the largest local count nothing is dropped
+    and the padded layout is the unpadded one (already pinned above) spread to
+    offsets e*C, with -1 padding rows after each segment."""
+    rng = np.random.default_rng(19)
+    for (T, E, k, lo, n) in [(50, 8, 2, 0, 8), (64, 16, 4, 3, 6), (33, 12, 3, 11, 1)]:
+        L = rng.integers(-3, 4, size=(T, E)).astype(np.float32)
+        idx, _ = O.topk_softmax(L, k)
+        cu, ou, pu, iu = O.local_dispatch(idx, E, lo, n)
+        cnt = np.diff(ou)
+        for C in (int(cnt.max()) if cnt.max() > 0 else 1, T):
+            cp, op, pp, ip = O.local_dispatch_padded(idx, E, lo, n, C)
+            assert np.array_equal(cp, cu)
+            assert op.tolist() == [e * C for e in range(n + 1)]
+            assert pp.shape == (n * C,)
+            for e in range(n):
+                seg = pp[e * C:(e + 1) * C]
+                assert np.array_equal(seg[:cnt[e]], pu[ou[e]:ou[e + 1]])
+                assert np.all(seg[cnt[e]:] == -1)
+            for a in range(T * k):
+                if iu[a] < 0:
+                    assert ip[a] == -1
+                else:
+                    e = int(idx.ravel()[a]) - lo
+                    assert ip[a] == e * C + iu[a] - ou[e]
+
+
+def pin_dispatch_padded_capacity(O):
+    """Small capacities: per expert the kept assignments are its C smallest
+    assignment ids (computed here by sorting each expert's ids), in ascending
+    order at the start of its segment; the rest of the segment is -1; perm and
+    inv are inverse on the kept set and inv is -1 elsewhere."""
+    rng = np.random.default_rng(23)
+    for (T, E, k, lo, n, C) in [(40, 6, 2, 0, 6, 3), (64, 16, 4, 3, 6, 5), (30, 4, 4, 0, 4, 1),
+                                (25, 8, 3, 2, 3, 7)]:
+        L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+        idx, _ = O.topk_softmax(L, k)
+        flat = idx.ravel().tolist()
+        counts, offsets, perm, inv = O.local_dispatch_padded(idx, E, lo, n, C)
+        assert counts.tolist() == [flat.count(e) for e in range(E)]
+        kept = set()
+        for e in range(n):
+            ids = sorted(a for a, x in enumerate(flat) if x == lo + e)[:C]
+            kept.update(ids)
+            seg = perm[e * C:(e + 1) * C].tolist()
+            assert seg[:len(ids)] == ids and all(v == -1 for v in seg[len(ids):])
+        for a in range(T * k):
+            if a in kept:
+                assert perm[inv[a]] == a
+            else:
+                assert inv[a] == -1
+        assert int((perm >= 0).sum()) == len(kept)
+
+
+def pin_gather_padded(O):
+    """Padding rows are all-zero bits; kept rows are copies of x[perm // k]."""
+    rng = np.random.default_rng(27)
+    x = rng.integers(1, 65535, size=(9, 16), dtype=np.uint16)
+    perm = np.array([5, -1, 17, -1, 8], dtype=np.int32)
+    got = O.gather_rows_padded(x, perm, 2)
+    want = np.stack([x[a // 2] if a >= 0 else np.zeros(16, np.uint16) for a in perm.tolist()])
+    assert np.array_equal(got, want)
+
+
 def pin_gather(O):
     rng = np.random.default_rng(17)
     x = rng.integers(0, 65535, size=(9, 16), dtype=np.uint16)
@@ -371,6 +435,29 @@ def pin_layer_rows_vs_tokens(O):
         toks = [0, 5, 17, 47]
         r = O.token_outputs(p, inp, o["topk_idx"], o["topk_w"], toks)
         assert np.allclose(r, o["y"][toks], rtol=2.0 ** -7 if dtype == "bf16" else 1e-12, atol=1e-300)
+
+
+def pin_layer_padded(O):
+    """The padded layer against the unpadded one: with C = the largest local
+    count the outputs agree; with a smaller C they agree with the unpadded
+    layer's packed rows combined without the dropped slots; padding rows of h
+    and y_packed are exact zeros."""
+    for dtype in ("f32", "bf16"):
+        p, inp = _small_layer(O, dtype)
+        u = O.moe_layer(p, inp)
+        cnt = np.diff(u["offsets"])
+        tol = 2.0 ** -7 if dtype == "bf16" else 1e-12
+        for C in (int(cnt.max()), max(1, int(cnt.max()) // 2)):
+            pd = O.moe_layer_padded(p, inp, C)
+            pad = pd["perm"] < 0
+            assert np.all(pd["h"][pad] == 0) and np.all(pd["y_packed"][pad] == 0)
+            kept = pd["inv"] >= 0
+            inv_u = np.where(kept, u["inv"], -1)
+            want = O.combine(u["y_packed"], inv_u, u["topk_w"], dtype)
+            assert np.allclose(pd["y"], want, rtol=tol, atol=1e-300)
+            if C == int(cnt.max()):
+                assert kept.sum() == (u["inv"] >= 0).sum()
+                assert np.allclose(pd["y"], u["y"], rtol=tol, atol=1e-300)
 
 
 def pin_skew_routing_shape(O):

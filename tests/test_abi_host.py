@@ -109,6 +109,28 @@ def test_workspace_checks():
     assert L.moe_workspace_bytes(ctypes.byref(p), 99) == 0
 
 
+def test_padded_calls_validate_capacity():
+    """capacity must lie in [1, T]; the padded dispatch needs its workspace
+    (the unpadded index plus the dispatch workspace); nothing is launched on
+    an error."""
+    p = _p()
+    L = M.lib()
+    need = L.moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_DISPATCH_PADDED)
+    assert need >= L.moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_DISPATCH) + 64 * 2 * 4
+    for cap in (0, -3, 65):
+        assert L.moe_dispatch_padded(ctypes.byref(p), cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, need, None) == M.MOE_ERR_INVALID_ARG
+        assert b"capacity" in L.moe_last_error()
+        assert L.moe_expert_gemm_padded(ctypes.byref(p), cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, None, 0, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_padded(ctypes.byref(p), 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, need - 1, None) == M.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch_padded(ctypes.byref(p), 8, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                                 FAKE, need, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_gemm_padded(ctypes.byref(p), 8, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                                    None, 0, None) == M.MOE_ERR_INVALID_ARG
+
+
 def test_write_logits_needs_buffer():
     p = _p(flags=M.MOE_F_WRITE_LOGITS)
     L = M.lib()

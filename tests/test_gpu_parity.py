@@ -180,6 +180,57 @@ def test_layer(name, overlap):
     check_close(O.widen(host(y), w.dtype), oref["y"], w.dtype, "y")
 
 
+# padded fixed-capacity layout (the A/B against the unpadded segments)
+PADDED = ["skew", "narrow_multiblock", "mixed_classes", "big_mixed", "fp32_mid", "one_local"]
+
+
+def _capacities(w, offsets):
+    """No-drop (largest count), dropping (half the mean count, and 1) and the
+    static worst case T."""
+    cnt = np.diff(offsets)
+    mx = max(1, int(cnt.max()) if cnt.size else 1)
+    mean = max(1, (w.T * w.k) // w.E)
+    return sorted({mx, max(1, mean // 2), 1, w.T})
+
+
+@pytest.mark.parametrize("name", PADDED)
+def test_dispatch_padded(name):
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, _ = M.route(p, d["x"], d["w_gate"], d["bias"])
+    idx_h = host(idx)
+    _, off_u, _, _ = O.local_dispatch(idx_h, w.E, w.expert_lo, w.n_local)
+    for C in _capacities(w, off_u):
+        o = M.dispatch_padded(p, C, idx, d["x"])
+        counts, offsets, perm, inv = O.local_dispatch_padded(idx_h, w.E, w.expert_lo, w.n_local, C)
+        assert np.array_equal(host(o["counts_all"]), counts), C
+        assert np.array_equal(host(o["offsets"]), offsets), C
+        assert np.array_equal(host(o["perm"]), perm), C
+        assert np.array_equal(host(o["inv"]), inv), C
+        assert np.array_equal(host(o["x_packed"]), O.gather_rows_padded(inp["x"], perm, w.k)), C
+
+
+@pytest.mark.parametrize("name", PADDED)
+def test_padded_layer(name):
+    """Padded dispatch, padded GEMM and combine against the oracle's padded
+    layer on the GPU's routing; padding rows of h and y_packed are zeros."""
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+    routing = {"topk_idx": host(idx), "topk_w": host(wt)}
+    _, off_u, _, _ = O.local_dispatch(routing["topk_idx"], w.E, w.expert_lo, w.n_local)
+    for C in _capacities(w, off_u):
+        o = M.dispatch_padded(p, C, idx, d["x"])
+        h, yp = M.expert_gemm_padded(p, C, o["x_packed"], o["offsets"], d["w1"], d["w3"], d["w2"])
+        y = M.combine(p, yp, o["inv"], wt, rows=w.n_local * C)
+        r = O.moe_layer_padded(w, inp, C, routing=routing)
+        pad = r["perm"] < 0
+        assert not np.any(host(h)[pad]) and not np.any(host(yp)[pad]), C
+        check_close(O.widen(host(h), w.dtype), r["h"], w.dtype, f"h C={C}")
+        check_close(O.widen(host(yp), w.dtype), r["y_packed"], w.dtype, f"y_packed C={C}")
+        check_close(O.widen(host(y), w.dtype), r["y"], w.dtype, f"y C={C}")
+
+
 def test_layer_deterministic_and_overlap_identical():
     import torch
     w, inp, ref, d = case("wide_dsv3_like")

@@ -114,7 +114,30 @@ def _combine_wrong_slot(y_packed, inv, topk_w, dtype):
     return _real["combine"](y_packed, inv, np.asarray(topk_w)[:, ::-1].copy(), dtype)
 
 
+def _dispatch_padded_keeps_last(topk_idx, E, lo, n, C):
+    """Keeps each expert's last C assignments instead of its first C."""
+    flat = np.asarray(topk_idx).ravel().astype(np.int64)
+    counts_all = np.bincount(flat, minlength=E).astype(np.int32)
+    perm = np.full(n * C, -1, dtype=np.int32)
+    inv = np.full(flat.shape[0], -1, dtype=np.int32)
+    for e in range(n):
+        ids = [a for a in range(flat.shape[0]) if flat[a] == lo + e][-C:]
+        for r, a in enumerate(ids):
+            perm[e * C + r] = a
+            inv[a] = e * C + r
+    return counts_all, (np.arange(n + 1) * C).astype(np.int32), perm, inv
+
+
+def _gather_padded_copies_row0(x, perm, k):
+    """Fills padding rows with x[0] instead of zeros."""
+    x = np.asarray(x)
+    perm = np.asarray(perm, dtype=np.int64)
+    return x[np.where(perm >= 0, perm, 0) // k]
+
+
 MUTATIONS = {
+    "dispatch_padded_keeps_last": ("local_dispatch_padded", _dispatch_padded_keeps_last),
+    "gather_padded_nonzero_padding": ("gather_rows_padded", _gather_padded_copies_row0),
     "round_half_away_from_zero": ("round_bf16", _round_half_away),
     "round_double_via_f32": ("round_bf16", _round_via_f32),
     "topk_ties_to_high_index": ("topk_softmax", _topk_ties_high),
