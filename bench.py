@@ -52,6 +52,11 @@ def parse():
                     help="A/B of the padded fixed-capacity dispatch against the unpadded "
                          "segments on the given workloads (default: the two skewed ones); "
                          "prints one JSON object per workload instead of the bench line")
+    ap.add_argument("--signal-ab", nargs=3, type=int, metavar=("M", "N", "K"),
+                    help="GEMM with per-tile completion signals: its rate, and GEMM-then-forward "
+                         "against the forwarder overlapped on a second stream; prints one JSON "
+                         "object instead of the bench line")
+    ap.add_argument("--forward-wg", type=int, default=16, help="tile forwarder workgroups")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no benchmark: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, "
                          "then WRITE_SIZE, --output-format csv) into "
@@ -294,8 +299,90 @@ def ab_padded(a):
         torch.cuda.empty_cache()
 
 
+def signal_ab(a):
+    """moe_gemm_signal at M x N x K (bf16): mean call time and MFMA fraction;
+    then the time from start to the last forwarded tile when the tile
+    forwarder (a.forward_wg workgroups) runs after the GEMM on the same stream
+    ("post-compute idle" before the transfer) and when it polls on a second
+    stream while the GEMM runs (each tile moves as soon as its flag lands)."""
+    import numpy as np
+    import torch
+
+    import combine_router_top_amd as M
+
+    Mr, N, K = a.signal_ab
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    A = torch.randn((Mr, K), generator=g, device="cuda").to(torch.bfloat16)
+    B = (torch.randn((K, N), generator=g, device="cuda") / K ** 0.5).to(torch.bfloat16)
+    C = torch.empty((Mr, N), dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(C)
+    tiles = M.gemm_signal_tiles(Mr, N)
+    flags = torch.zeros(tiles, dtype=torch.int32, device="cuda")
+    timeouts = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    epoch = [0]
+
+    def nxt():
+        epoch[0] += 1
+        return epoch[0]
+
+    spin = 1 << 24
+    res = {"M": Mr, "N": N, "K": K, "tiles": tiles, "forward_workgroups": a.forward_wg}
+    # GEMM alone
+    for _ in range(2):
+        M.gemm_signal(A, B, flags, nxt(), stream=s1, out=C)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(s1)
+    for _ in range(a.steps):
+        M.gemm_signal(A, B, flags, nxt(), stream=s1, out=C)
+    e1.record(s1)
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / a.steps
+    flops = 2.0 * Mr * N * K
+    res["gemm_us"] = gemm_ms * 1e3
+    res["gemm_tflops"] = flops / (gemm_ms * 1e-3) / 1e12
+    res["gemm_mfma_frac"] = res["gemm_tflops"] * 1e12 / MFMA_PEAK["bf16"]
+    # sequential: forward after the whole GEMM, same stream
+    seq = []
+    for it in range(a.steps + 2):
+        ep = nxt()
+        b0, b1 = ev(), ev()
+        b0.record(s1)
+        M.gemm_signal(A, B, flags, ep, stream=s1, out=C)
+        M.tile_forward(C, dst, flags, ep, spin, timeouts, workgroups=a.forward_wg, stream=s1)
+        b1.record(s1)
+        torch.cuda.synchronize()
+        if it >= 2:
+            seq.append(b0.elapsed_time(b1))
+    # overlapped: the forwarder polls on s2 while the GEMM runs on s1
+    ovl = []
+    for it in range(a.steps + 2):
+        ep = nxt()
+        b0, b1, b2 = ev(), ev(), ev()
+        b0.record(s1)
+        s2.wait_event(b0)
+        M.tile_forward(C, dst, flags, ep, spin, timeouts, workgroups=a.forward_wg, stream=s2)
+        M.gemm_signal(A, B, flags, ep, stream=s1, out=C)
+        b1.record(s1)
+        b2.record(s2)
+        torch.cuda.synchronize()
+        if it >= 2:
+            ovl.append(max(b0.elapsed_time(b1), b0.elapsed_time(b2)))
+    res["forward_after_gemm_us"] = float(np.mean(seq)) * 1e3
+    res["forward_overlapped_us"] = float(np.mean(ovl)) * 1e3
+    res["timeouts"] = int(timeouts.item())
+    res["exact_copy"] = bool(torch.equal(dst, C))
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
+    if a.signal_ab is not None:
+        signal_ab(a)
+        return
     if a.write_traffic:
         write_traffic(a)
         return

@@ -14,6 +14,8 @@ Functions (same names as the C calls):
     layer(p, x, w_gate, bias, w1, w3, w2, routing=False, overlap=False, ...) -> y or (y, dict)
     dispatch_padded(p, capacity, topk_idx, x) -> dict(counts_all, offsets, perm, inv, x_packed)
     expert_gemm_padded(p, capacity, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
+    gemm_signal(A, B, flags, epoch) -> C          (C = rnd(A B), a flag per 256 x 256 tile)
+    tile_forward(C, dst, flags, epoch, spin_limit, timeouts, workgroups)
 """
 from __future__ import annotations
 
@@ -30,10 +32,11 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_F_WRITE_LOGITS, MOE_F_OVERLAP = 1, 2
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_EXPERT_GEMM, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
 MOE_CALL_DISPATCH_PADDED, MOE_CALL_EXPERT_GEMM_PADDED = 5, 6
+MOE_SCOPE_AGENT, MOE_SCOPE_SYSTEM = 0, 1
 
 EXPORTED = ["moe_last_error", "moe_version", "moe_workspace_bytes", "moe_route", "moe_dispatch",
             "moe_expert_gemm", "moe_combine", "moe_layer", "moe_dispatch_padded",
-            "moe_expert_gemm_padded"]
+            "moe_expert_gemm_padded", "moe_gemm_signal_tiles", "moe_gemm_signal", "moe_tile_forward"]
 
 
 class MoeError(RuntimeError):
@@ -77,8 +80,14 @@ def lib() -> ctypes.CDLL:
                                 vp, vp]
         L.moe_dispatch_padded.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_expert_gemm_padded.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_gemm_signal_tiles.argtypes = [i32, i32]
+        L.moe_gemm_signal_tiles.restype = ctypes.c_int64
+        u32 = ctypes.c_uint32
+        L.moe_gemm_signal.argtypes = [i32, i32, i32, vp, vp, vp, vp, u32, i32, vp]
+        L.moe_tile_forward.argtypes = [i32, i32, vp, vp, vp, u32, u32, i32, vp, i32, vp]
         for n in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_layer",
-                  "moe_dispatch_padded", "moe_expert_gemm_padded"):
+                  "moe_dispatch_padded", "moe_expert_gemm_padded", "moe_gemm_signal",
+                  "moe_tile_forward"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -309,6 +318,46 @@ def expert_gemm_padded(p: Spec, capacity: int, x_packed, offsets, w1, w3, w2, wo
                                         _ptr(yp), _ptr(ws), 0 if ws is None else ws.numel(),
                                         _stream(stream)))
     return h, yp
+
+
+def gemm_signal_tiles(M: int, N: int) -> int:
+    n = int(lib().moe_gemm_signal_tiles(int(M), int(N)))
+    if n <= 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, lib().moe_last_error().decode())
+    return n
+
+
+def gemm_signal(A, B, flags, epoch: int, scope: int = MOE_SCOPE_AGENT, stream=None, out=None):
+    """C = rnd(A B) (bf16 [M,K] x [K,N]); flags (int32 or uint32 device
+    tensor of gemm_signal_tiles(M, N) entries) receive `epoch` per finished
+    256 x 256 tile."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[1]
+    _need(A, (M, K), torch.bfloat16, "A")
+    _need(B, (K, N), torch.bfloat16, "B")
+    _need(flags, (gemm_signal_tiles(M, N),), flags.dtype, "flags")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if out is None else out
+    _need(C, (M, N), torch.bfloat16, "C")
+    _check(lib().moe_gemm_signal(M, N, K, _ptr(A), _ptr(B), _ptr(C), _ptr(flags), int(epoch),
+                                 int(scope), _stream(stream)))
+    return C
+
+
+def tile_forward(C, dst, flags, epoch: int, spin_limit: int, timeouts, workgroups: int = 4,
+                 scope: int = MOE_SCOPE_AGENT, stream=None):
+    """Copies each 256 x 256 tile of C to dst once flags[tile] == epoch;
+    adds 1 to timeouts[0] per tile whose flag did not arrive in spin_limit polls."""
+    torch = _torch()
+    M, N = C.shape
+    _need(C, (M, N), torch.bfloat16, "C")
+    _need(dst, (M, N), torch.bfloat16, "dst")
+    _need(flags, (gemm_signal_tiles(M, N),), flags.dtype, "flags")
+    _need(timeouts, (1,), timeouts.dtype, "timeouts")
+    _check(lib().moe_tile_forward(M, N, _ptr(C), _ptr(dst), _ptr(flags), int(epoch),
+                                  int(spin_limit), int(scope), _ptr(timeouts), int(workgroups),
+                                  _stream(stream)))
+    return dst
 
 
 def layer(p: Spec, x, w_gate, bias, w1, w3, w2, routing: bool = False, want_logits: bool = False,

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "tile_forward.hip", "moe_api.cpp"]
 
 
 def hipcc() -> str:

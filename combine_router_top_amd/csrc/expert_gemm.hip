@@ -609,6 +609,56 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
 }
 
 // ---------------------------------------------------------------------------
+// GEMM with a completion signal per output tile: the compute half of the
+// pages' GEMM + AllGather workload ("CUCo", Table 4, row "GEMM + AllGather":
+// the broadcast starts from the device right after the GEMM, instead of the
+// GPU idling until a host-launched collective).  C[M,N] = rnd(A[M,K] B[K,N]),
+// bf16, fp32 accumulation, on the 256 x 256 large-tile core; once a tile's
+// stores are complete and visible at the requested scope, flags[tile] is set
+// to `epoch` with a release store, so a consumer (a tile forwarder, locally
+// moe_tile_forward) can move each tile as soon as it exists.  Tiles are
+// numbered row-major over ceil(M / 256) x ceil(N / 256); with epochs the flag
+// array never needs clearing between calls.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * XB_NW, 1) void gemm_signal_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C, int M,
+    int N, int K, int ntn, uint32_t* __restrict__ flags, uint32_t epoch, int system_scope) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
+  const int tile = blockIdx.x;
+  const int tm = tile / ntn;
+  BigTile bt;
+  bt.e = 0;
+  bt.r0 = tm * XB_BM;
+  bt.R = min(XB_BM, M - bt.r0);
+  bt.nt = tile - tm * ntn;
+  big_tile<false>(A, B, nullptr, K, N, C, bt, RowMap{nullptr, 1, 0}, As, Bs);
+  // every thread's stores of the tile complete and visible at the scope,
+  // then one release store of the flag
+  if (system_scope) __threadfence_system();
+  else __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (system_scope) __hip_atomic_store(flags + tile, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    else __hip_atomic_store(flags + tile, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+int64_t gemm_signal_tiles(int M, int N) {
+  return (int64_t)((M + XB_BM - 1) / XB_BM) * ((N + XB_BN - 1) / XB_BN);
+}
+
+hipError_t launch_gemm_signal(int M, int N, int K, const void* A, const void* B, void* C,
+                              uint32_t* flags, uint32_t epoch, int system_scope, hipStream_t st) {
+  const int ntn = (N + XB_BN - 1) / XB_BN;
+  const int64_t tiles = gemm_signal_tiles(M, N);
+  hipLaunchKernelGGL(gemm_signal_kernel, dim3((unsigned)tiles), dim3(64 * XB_NW), 0, st,
+                     (const bf16_t*)A, (const bf16_t*)B, (bf16_t*)C, M, N, K, ntn, flags, epoch,
+                     system_scope);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fp32: one thread per output element
 // ---------------------------------------------------------------------------
 template <bool SWIGLU>

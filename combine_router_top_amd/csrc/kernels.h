@@ -40,6 +40,15 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                               void* y_packed, void* ws, int e_begin, int e_end, hipStream_t st,
                               const int32_t* perm = nullptr);
 
+// expert_gemm.hip: GEMM C = rnd(A B) with a release flag per 256 x 256 tile
+int64_t gemm_signal_tiles(int M, int N);
+hipError_t launch_gemm_signal(int M, int N, int K, const void* A, const void* B, void* C,
+                              uint32_t* flags, uint32_t epoch, int system_scope, hipStream_t st);
+// tile_forward.hip: copy each tile of C to dst once its flag reads epoch
+hipError_t launch_tile_forward(int M, int N, const void* C, void* dst, const uint32_t* flags,
+                               uint32_t epoch, uint32_t spin_limit, int system_scope,
+                               uint32_t* timeouts, int workgroups, hipStream_t st);
+
 // combine.hip
 hipError_t launch_combine(const Prob& p, const void* y_packed, const int32_t* inv,
                           const float* w, void* y, hipStream_t st);

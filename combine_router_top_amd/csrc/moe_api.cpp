@@ -146,6 +146,20 @@ moe_status_t check_capacity(const moe::Prob& q, int32_t capacity) {
   return MOE_OK;
 }
 
+// Shapes of the signalled GEMM: bf16 row-major A [M,K], B [K,N], C [M,N];
+// N and K multiples of 8 (16-byte rows), B below 2 GiB and A's 256-row
+// blocks below 4 GiB (32-bit buffer descriptors), M*N addressable.
+moe_status_t check_signal_shape(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "M=%d N=%d K=%d must be positive", M, N, K);
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "N=%d and K=%d must be multiples of 8", N, K);
+  if ((int64_t)K * N * 2 >= ((int64_t)1 << 31) || (int64_t)256 * K * 2 >= ((int64_t)1 << 32) ||
+      (int64_t)M * N >= ((int64_t)1 << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "GEMM too large (M=%d N=%d K=%d)", M, N, K);
+  return MOE_OK;
+}
+
 moe_status_t hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -311,6 +325,57 @@ moe_status_t moe_expert_gemm_padded(const moe_problem_t* p, int32_t capacity, co
   return hip_status(moe::launch_expert_gemm(q, x_packed, offsets, w1, w3, w2, h, y_packed, workspace,
                                             0, q.n, (hipStream_t)stream),
                     "moe_expert_gemm_padded");
+}
+
+int64_t moe_gemm_signal_tiles(int32_t M, int32_t N) {
+  if (M <= 0 || N <= 0) {
+    fail(MOE_ERR_INVALID_ARG, "M=%d and N=%d must be positive", M, N);
+    return 0;
+  }
+  ok();
+  return moe::gemm_signal_tiles(M, N);
+}
+
+moe_status_t moe_gemm_signal(int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C,
+                             uint32_t* flags, uint32_t epoch, int32_t scope, void* stream) {
+  moe_status_t st;
+  if ((st = check_signal_shape(M, N, K)) != MOE_OK) return st;
+  NEED_PTR(A);
+  NEED_PTR(B);
+  NEED_PTR(C);
+  NEED_PTR(flags);
+  NEED_ALIGNED(A);
+  NEED_ALIGNED(B);
+  NEED_ALIGNED(C);
+  if (epoch == 0) return fail(MOE_ERR_INVALID_ARG, "epoch must be nonzero");
+  if (scope != MOE_SCOPE_AGENT && scope != MOE_SCOPE_SYSTEM)
+    return fail(MOE_ERR_INVALID_ARG, "scope %d is neither MOE_SCOPE_AGENT nor MOE_SCOPE_SYSTEM", scope);
+  (void)hipGetLastError();
+  return hip_status(moe::launch_gemm_signal(M, N, K, A, B, C, flags, epoch, scope, (hipStream_t)stream),
+                    "moe_gemm_signal");
+}
+
+moe_status_t moe_tile_forward(int32_t M, int32_t N, const void* C, void* dst, const uint32_t* flags,
+                              uint32_t epoch, uint32_t spin_limit, int32_t scope, uint32_t* timeouts,
+                              int32_t workgroups, void* stream) {
+  moe_status_t st;
+  if ((st = check_signal_shape(M, N, 8)) != MOE_OK) return st;
+  NEED_PTR(C);
+  NEED_PTR(dst);
+  NEED_PTR(flags);
+  NEED_PTR(timeouts);
+  NEED_ALIGNED(C);
+  NEED_ALIGNED(dst);
+  if (epoch == 0) return fail(MOE_ERR_INVALID_ARG, "epoch must be nonzero");
+  if (spin_limit == 0) return fail(MOE_ERR_INVALID_ARG, "spin_limit must be positive");
+  if (scope != MOE_SCOPE_AGENT && scope != MOE_SCOPE_SYSTEM)
+    return fail(MOE_ERR_INVALID_ARG, "scope %d is neither MOE_SCOPE_AGENT nor MOE_SCOPE_SYSTEM", scope);
+  if (workgroups <= 0 || workgroups > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "workgroups=%d outside [1, 1024]", workgroups);
+  (void)hipGetLastError();
+  return hip_status(moe::launch_tile_forward(M, N, C, dst, flags, epoch, spin_limit, scope, timeouts,
+                                             workgroups, (hipStream_t)stream),
+                    "moe_tile_forward");
 }
 
 moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int32_t* inv,

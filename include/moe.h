@@ -17,6 +17,9 @@
  *   moe_layer        all of the above, stream-ordered
  *   moe_dispatch_padded, moe_expert_gemm_padded
  *                    the padded fixed-capacity layout, as an A/B
+ *   moe_gemm_signal, moe_tile_forward
+ *                    GEMM with per-tile completion flags and their consumer
+ *                    (the local half of the pages' GEMM + AllGather)
  *
  * The pages state no formulas; the definitions below are the plain MoE layer
  * (softmax top-k gating renormalised over the selected k, ties to the lower
@@ -222,6 +225,41 @@ moe_status_t moe_expert_gemm_padded(const moe_problem_t* p, int32_t capacity, co
                                     const int32_t* offsets, const void* w1, const void* w3,
                                     const void* w2, void* h, void* y_packed, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * GEMM with per-tile completion signals: the local compute half of the pages'
+ * GEMM + AllGather workload (CUCo, Table 4, row "GEMM + AllGather": a
+ * device-initiated broadcast fused right after GEMM completion instead of a
+ * host-launched collective after the whole GEMM).
+ *   C[M,N] = rnd(A[M,K] B[K,N]), bf16 row-major, fp32 accumulation, RNE.
+ * C is computed in 256 x 256 tiles numbered row-major over
+ * ceil(M/256) x ceil(N/256) (moe_gemm_signal_tiles(M, N) of them).  When a
+ * tile's stores are complete and visible at `scope` (MOE_SCOPE_AGENT: this
+ * GPU; MOE_SCOPE_SYSTEM: also peers and host, which adds an L2 write-back),
+ * flags[tile] is set to `epoch` by a release store.  `epoch` must be nonzero
+ * and differ from what flags holds before the call (a zeroed array and
+ * increasing epochs never need clearing).  N, K multiples of 8; K*N*2 < 2^31.
+ */
+enum { MOE_SCOPE_AGENT = 0, MOE_SCOPE_SYSTEM = 1 };
+int64_t moe_gemm_signal_tiles(int32_t M, int32_t N);
+moe_status_t moe_gemm_signal(int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C,
+                             uint32_t* flags, uint32_t epoch, int32_t scope, void* stream);
+
+/*
+ * Tile forwarder, the consumer of moe_gemm_signal's flags (where the
+ * broadcast of GEMM + AllGather would start; dst can be any device-visible
+ * buffer).  Workgroup g of `workgroups` takes tiles g, g + workgroups, ...;
+ * for each it polls flags[tile] with acquire loads at `scope`, at most
+ * spin_limit times with a short sleep in between, then copies the tile of C
+ * (same geometry as moe_gemm_signal) to dst, or, if the flag never read
+ * `epoch`, adds 1 to *timeouts (a device counter the caller zeroes) and moves
+ * on: the call always finishes.  Run concurrently with moe_gemm_signal on
+ * another stream, keep `workgroups` small: polling workgroups hold compute
+ * units.
+ */
+moe_status_t moe_tile_forward(int32_t M, int32_t N, const void* C, void* dst, const uint32_t* flags,
+                              uint32_t epoch, uint32_t spin_limit, int32_t scope, uint32_t* timeouts,
+                              int32_t workgroups, void* stream);
 
 /*
  * The whole layer: moe_route, moe_dispatch, moe_expert_gemm, moe_combine in

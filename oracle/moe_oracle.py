@@ -57,6 +57,7 @@ __all__ = [
     "combine",
     "moe_layer",
     "moe_layer_padded",
+    "gemm",
     "token_outputs",
 ]
 
@@ -322,6 +323,13 @@ def moe_layer_padded(p, inputs: Dict[str, np.ndarray], capacity: int,
     out["h"], out["y_packed"] = h, yp
     out["y"] = combine(yp, inv, w, p.dtype)
     return out
+
+
+def gemm(A: np.ndarray, B: np.ndarray, dtype: str) -> np.ndarray:
+    """C = rnd(A B): the plain product of the GEMM + AllGather workload's
+    compute half (CUCo, Table 4, row "GEMM + AllGather"), float64, rounded once
+    to the storage dtype."""
+    return rnd(widen(A, dtype) @ widen(B, dtype), dtype)
 
 
 def token_outputs(p, inputs: Dict[str, np.ndarray], topk_idx: np.ndarray, topk_w: np.ndarray,

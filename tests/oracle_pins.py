@@ -460,6 +460,36 @@ def pin_layer_padded(O):
                 assert np.allclose(pd["y"], u["y"], rtol=tol, atol=1e-300)
 
 
+def pin_gemm_integer_exact(O):
+    """Integer-valued bf16 operands: the product equals numpy's int64 matmul
+    and, where it is exactly representable in bf16 (|v| <= 256), rnd keeps it."""
+    rng = np.random.default_rng(37)
+    for (M, K, N) in [(5, 8, 3), (17, 40, 24), (1, 8, 8)]:
+        a = rng.integers(-2, 3, size=(M, K))
+        b = rng.integers(-2, 3, size=(K, N))
+        store = lambda v: (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        c = O.gemm(store(a), store(b), "bf16")
+        ref = (a.astype(np.int64) @ b.astype(np.int64)).astype(np.float64)
+        small = np.abs(ref) <= 256
+        assert np.array_equal(c[small], ref[small])
+        assert np.allclose(c, ref, rtol=2.0 ** -8, atol=0)
+        c32 = O.gemm(a.astype(np.float32), b.astype(np.float32), "f32")
+        assert np.array_equal(c32, ref)
+
+
+def pin_gemm_vs_torch(O):
+    """Random bf16 operands: float64 product equals torch's float64 matmul (a
+    library routine) before rounding, and rnd is the bf16 rounding pinned above."""
+    import torch
+    rng = np.random.default_rng(41)
+    a = (rng.standard_normal((33, 72)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    b = (rng.standard_normal((72, 40)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ta = torch.from_numpy(O.widen(a, "bf16"))
+    tb = torch.from_numpy(O.widen(b, "bf16"))
+    exact = (ta @ tb).numpy()
+    assert np.array_equal(O.gemm(a, b, "bf16"), O.round_bf16(exact))
+
+
 def pin_skew_routing_shape(O):
     """With the Zipf-like bias b[e] = 1.5 ln(1/(e+1)) the low experts receive
     far more than the mean count and some experts receive none."""

@@ -131,6 +131,32 @@ def test_padded_calls_validate_capacity():
                                     None, 0, None) == M.MOE_ERR_INVALID_ARG
 
 
+def test_signal_calls_validate():
+    """Shapes, pointers, epoch, scope, spin limit and workgroup count are
+    checked on the host; nothing is launched on an error."""
+    L = M.lib()
+    assert L.moe_gemm_signal_tiles(300, 520) == 2 * 3
+    assert L.moe_gemm_signal_tiles(0, 8) == 0
+    ok = dict(M=300, N=520, K=264)
+    def sig(M=300, N=520, K=264, A=FAKE, B=FAKE, C=FAKE, flags=FAKE, epoch=1, scope=0):
+        return L.moe_gemm_signal(M, N, K, A, B, C, flags, epoch, scope, None)
+    assert sig(M=0) == M.MOE_ERR_INVALID_ARG
+    assert sig(N=100) == M.MOE_ERR_UNSUPPORTED
+    assert sig(K=12) == M.MOE_ERR_UNSUPPORTED
+    assert sig(K=1 << 20, N=1 << 11) == M.MOE_ERR_UNSUPPORTED   # B >= 2 GiB
+    assert sig(flags=0) == M.MOE_ERR_INVALID_ARG
+    assert sig(A=FAKE + 2) == M.MOE_ERR_UNSUPPORTED
+    assert sig(epoch=0) == M.MOE_ERR_INVALID_ARG
+    assert sig(scope=2) == M.MOE_ERR_INVALID_ARG
+    def fwd(spin=100, wg=4, epoch=1, timeouts=FAKE, scope=0):
+        return L.moe_tile_forward(300, 520, FAKE, FAKE, FAKE, epoch, spin, scope, timeouts, wg, None)
+    assert fwd(spin=0) == M.MOE_ERR_INVALID_ARG
+    assert fwd(wg=0) == M.MOE_ERR_INVALID_ARG and fwd(wg=2000) == M.MOE_ERR_INVALID_ARG
+    assert fwd(epoch=0) == M.MOE_ERR_INVALID_ARG
+    assert fwd(timeouts=0) == M.MOE_ERR_INVALID_ARG
+    assert fwd(scope=-1) == M.MOE_ERR_INVALID_ARG
+
+
 def test_write_logits_needs_buffer():
     p = _p(flags=M.MOE_F_WRITE_LOGITS)
     L = M.lib()

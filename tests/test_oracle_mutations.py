@@ -135,7 +135,14 @@ def _gather_padded_copies_row0(x, perm, k):
     return x[np.where(perm >= 0, perm, 0) // k]
 
 
+def _gemm_not_rounded(A, B, dtype):
+    """Skips the rounding to the storage dtype."""
+    from oracle.moe_oracle import widen
+    return widen(A, dtype) @ widen(B, dtype)
+
+
 MUTATIONS = {
+    "gemm_not_rounded": ("gemm", _gemm_not_rounded),
     "dispatch_padded_keeps_last": ("local_dispatch_padded", _dispatch_padded_keeps_last),
     "gather_padded_nonzero_padding": ("gather_rows_padded", _gather_padded_copies_row0),
     "round_half_away_from_zero": ("round_bf16", _round_half_away),
