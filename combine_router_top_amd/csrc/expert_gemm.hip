@@ -295,15 +295,15 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
 constexpr int XB_BM = 256;
 constexpr int XB_BN = XT_BN;    // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
 constexpr int XB_NW = 8;        // waves per workgroup
-constexpr int XB_TH = 320;      // row count from which an expert uses this kernel
+#ifndef MOE_XB_TH
+#define MOE_XB_TH 320
+#endif
+constexpr int XB_TH = MOE_XB_TH; // row count from which an expert uses this kernel
 #ifndef MOE_XB_GM
 #define MOE_XB_GM 8
 #endif
 constexpr int XB_GM = MOE_XB_GM; // m-tiles grouped together along the XCD-local order
-// Large-tile workgroups per compute unit when few or no segments reach XB_TH.
-#ifndef MOE_XB_SPARSE_WG
-#define MOE_XB_SPARSE_WG 4
-#endif
+
 
 struct BigTile {
   int e, r0, R, nt;
@@ -570,10 +570,9 @@ __device__ __forceinline__ void big_tile(const bf16_t* __restrict__ A, const bf1
 // The tile order is cut into 8 contiguous ranges, one per XCD (workgroup id
 // mod 8 on this part); workgroup (x, q) of the G = gridDim.x takes tiles
 // q, q + G/8, ... of range x, so the tiles of a range start in order and
-// neighbouring tiles share operands in that XCD's L2.  With G at least 8 times
-// the largest range every workgroup takes at most one tile and the hardware
-// balances the compute units; a smaller G makes the launch cheap when there are
-// few or no large segments.
+// neighbouring tiles share operands in that XCD's L2.  The host sizes G to
+// cover every tile, so each workgroup takes at most one and the hardware
+// balances the compute units.
 template <bool SWIGLU>
 __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int e_begin, int e_end,
@@ -712,9 +711,15 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     // with perm, x_packed is x itself and GEMM-1 reads row perm[p] / k for packed row p
     const RowMap rm1 = perm ? RowMap{perm, p.k, (uint32_t)((int64_t)p.T * p.d * 2)} : RowMap{nullptr, 1, 0};
     const RowMap rm2{nullptr, 1, 0};
-    // experts with >= XB_TH rows go to the 256 x 256 kernel; no expert can
-    // exceed T rows (top-k picks distinct experts), so small T never needs it
-    const bool big = p.T >= XB_TH;
+    // Dense-like routing (the mean segment reaches XB_TH rows, or every
+    // segment does in the padded layout): experts with >= XB_TH rows go to the
+    // 256 x 256 kernel.  Otherwise every segment, however long, streams
+    // through the thin/medium tiles in one launch: a few long segments of a
+    // skewed routing balance better there than in a second, serialized
+    // launch (4096-token Zipf-skewed routing: 3.07 against 3.52 ms), and a
+    // sparse routing skips the large-tile launches altogether.
+    const bool dense_like = p.seg_rows ? p.seg_rows >= XB_TH : (int64_t)p.T * p.k >= (int64_t)XB_TH * p.E;
+    const bool big = dense_like && p.T >= XB_TH;
     const int th = big ? XB_TH : INT32_MAX;
     const int ne = e_end - e_begin;
     // Medium column blocks: when the expected segment is a single medium row
@@ -754,18 +759,12 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
       return (unsigned)(8 * ((((w + 7) / 8) + wmin - 1) / wmin));
     };
     const int mc1 = pick_mcols(2 * p.f), mc2 = pick_mcols(p.d);
-    // Large-tile grid.  Its tiles: sum over experts with n_e >= XB_TH of
-    // ceil(n_e / BM) <= rows_max / BM + min(ne, rows_max / XB_TH) m-tiles, times
-    // ntn.  When the mean segment reaches XB_TH rows (dense-like routing) the
-    // grid covers every tile with its own workgroup; otherwise there are few
-    // or no large segments and at most 4 workgroups per compute unit loop over
-    // them, which keeps an empty launch short.
+    // Large-tile grid (dense-like routing only): its tiles, the sum over
+    // experts with n_e >= XB_TH of ceil(n_e / BM) <= rows_max / BM +
+    // min(ne, rows_max / XB_TH) m-tiles, times ntn, each with its own
+    // workgroup.
     const int64_t bblocks = (p.rows_max + XB_BM - 1) / XB_BM + std::min<int64_t>(ne, p.rows_max / XB_TH);
-    const bool dense_like = p.seg_rows ? p.seg_rows >= XB_TH : (int64_t)p.T * p.k >= (int64_t)XB_TH * p.E;
-    auto big_grid = [&](int ntn) {
-      const int64_t w = bblocks * ntn;
-      return (unsigned)(dense_like ? w : std::min<int64_t>(w, MOE_XB_SPARSE_WG * (int64_t)big_cus()));
-    };
+    auto big_grid = [&](int ntn) { return (unsigned)(bblocks * ntn); };
     hipError_t e;
     if (big) {
       const int ntn = (p.f + 127) / 128;

@@ -31,9 +31,13 @@ SMALL = {
     "k_equals_e": W("k_equals_e", 90, 64, 6, 6, 48, 1, 4, "bf16", seed=12),
     # large segments (256 x 256 tile kernel) with row, K and N tails
     "big_tails": W("big_tails", 1500, 328, 4, 2, 264, 0, 4, "bf16", seed=14),
-    # skewed: some experts on the large-tile kernel, the rest streamed
+    # skewed, not dense-like (mean 300 rows): every segment, up to ~1000 rows,
+    # streams through the thin/medium tiles in one launch
     "big_mixed": W("big_mixed", 1200, 256, 16, 4, 256, 0, 8, "bf16", skew=True, seed=15),
-    # all three tile classes (thin <= 48 rows, medium, large >= 320) with column tails
+    # skewed and dense-like (mean 500 rows): segments of 35 .. 1736 rows, the
+    # ones >= 320 on the large-tile kernel next to thin and medium ones
+    "big_dense_skew": W("big_dense_skew", 2000, 256, 8, 2, 256, 0, 8, "bf16", skew=True, seed=19),
+    # thin (<= 48 rows) and medium segments, some past 320 rows, with column tails
     "mixed_classes": W("mixed_classes", 700, 264, 24, 4, 328, 0, 12, "bf16", skew=True, seed=16),
     # ~60 rows per expert on 16 local experts: the host narrows the medium
     # column blocks so that they fill the last round of workgroups (GEMM-2:
