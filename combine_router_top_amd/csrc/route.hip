@@ -16,9 +16,11 @@
 //                       in flight.  HBM-bound on x.
 //   router_plain        any dtype/shape: one thread per logit (fp32 problems
 //                       and shapes the MFMA kernels do not cover).
-//   topk_softmax_kernel one wave per token: sums the K splits in fixed order,
-//                       adds the bias, optionally stores the logits, then k
-//                       rounds of a wave-wide max over (value, index) keys.
+//   topk_softmax_kernel one wave per token: sums the K splits in fixed order
+//                       (loads of 8 splits x all of a lane's experts in
+//                       flight together), adds the bias, optionally stores
+//                       the logits, then k rounds of a wave-wide max over
+//                       (value, index) keys.
 #include "common.h"
 #include "gemm_core.h"
 #include "kernels.h"
@@ -262,28 +264,44 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // sum each expert's K splits in ascending order; the loads of 8 splits of
+  // all NV experts of the lane are issued together (one round trip per 8
+  // splits, not per expert and 8 splits)
+  const int64_t sstride = (int64_t)T * E;
+  const float* pt = part + (int64_t)t * E + lane;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = lane + 64 * j < E ? pt[64 * j] : 0.f;
+  int s = 1;
+  for (; s + 8 <= nsplit; s += 8) {
+    float q[NV][8];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        q[j][u] = lane + 64 * j < E ? pt[(int64_t)(s + u) * sstride + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[j] += q[j][u];
+  }
+  for (; s < nsplit; ++s) {
+    float q[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) q[j] = lane + 64 * j < E ? pt[(int64_t)s * sstride + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] += q[j];
+  }
   uint64_t key[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     key[j] = 0;
     const int e = lane + 64 * j;
     if (e < E) {
-      // sum the K splits in ascending order; loads issued 8 at a time
-      const float* pe = part + (int64_t)t * E + e;
-      const int64_t sstride = (int64_t)T * E;
-      float v = pe[0];
-      int s = 1;
-      for (; s + 8 <= nsplit; s += 8) {
-        float q[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = pe[(int64_t)(s + u) * sstride];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v += q[u];
-      }
-      for (; s < nsplit; ++s) v += pe[(int64_t)s * sstride];
-      if (bias) v += bias[e];
-      if (logits_out) logits_out[(int64_t)t * E + e] = v;
-      key[j] = ((uint64_t)f32_order_key(v) << 32) | (uint32_t)(1023 - e);
+      float vj = v[j];
+      if (bias) vj += bias[e];
+      if (logits_out) logits_out[(int64_t)t * E + e] = vj;
+      key[j] = ((uint64_t)f32_order_key(vj) << 32) | (uint32_t)(1023 - e);
     }
   }
   float myv = 0.f, v0 = 0.f;
