@@ -39,6 +39,10 @@ SMALL = {
     "big_dense_skew": W("big_dense_skew", 2000, 256, 8, 2, 256, 0, 8, "bf16", skew=True, seed=19),
     # thin (<= 48 rows) and medium segments, some past 320 rows, with column tails
     "mixed_classes": W("mixed_classes", 700, 264, 24, 4, 328, 0, 12, "bf16", skew=True, seed=16),
+    # more than 8 local slots per token (combine loads slots in groups of 8):
+    # k = 16 and the maximum k = 32, all experts local
+    "many_slots_k16": W("many_slots_k16", 200, 136, 32, 16, 64, 0, 32, "bf16", seed=20),
+    "many_slots_k32": W("many_slots_k32", 96, 64, 64, 32, 40, 0, 64, "bf16", seed=21),
     # ~60 rows per expert on 16 local experts: the host narrows the medium
     # column blocks so that they fill the last round of workgroups (GEMM-2:
     # 7168 columns in 448-column blocks; GEMM-1: 2 x 3072 weight columns in
