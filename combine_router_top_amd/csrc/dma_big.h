@@ -1,0 +1,230 @@
+// Large expert-GEMM tiles fed by buffer loads that write straight into LDS
+// (gfx950): 256 rows of A against a 256-column block of a row-major [K][N]
+// bf16 matrix B, 8 waves (two per SIMD).  Used where a segment is long enough
+// for the product to be bound by the matrix cores rather than by the weight
+// stream (dense routing), and by the GEMM with per-tile completion flags.
+//
+// Per 32-K stage the waves copy the weight block as two half-panels of 32 rows
+// x 128 columns (GEMM-1: the W1 columns and the same W3 columns of 128 h
+// columns; GEMM-2: two neighbouring 128-column halves of W2) and the stage's
+// 32 K of all 256 A rows, each wave with two weight and two A copy
+// instructions of 16 bytes per lane (weight copies read four 256-byte row
+// runs, A copies sixteen 64-byte runs).  No register holds the data in transit
+// and no instruction rewrites it.  The ring has BD_NS slots of 32 KB, so
+// BD_NS - 1 stages are in flight while one is multiplied; a stage is released
+// by an explicit wait for the wave's own copies and one barrier (the
+// copy/wait/barrier protocol of dma_tile.h).
+//
+// Wave w = (wm, wn) = (w & 3, w >> 2) multiplies rows 64 wm .. 64 wm + 63 by
+// 128 weight columns: GEMM-1 h columns 64 wn .. 64 wn + 63 of W1 (n-tiles
+// 0..3) and of W3 (n-tiles 4..7), GEMM-2 half-panel wn (n-tiles 0..7).  The
+// MFMA takes the weights as its 16-row operand: a lane's weight fragment (8
+// consecutive k of one column) is two ds_read_b64_tr_b16 reads of the
+// row-major half-panel, its A fragment one 16-byte read.  A product lane then
+// holds 4 consecutive output columns of one row (8-byte stores), and the W1
+// and W3 products of one h column sit in the same lane.
+//
+// LDS swizzle (16-byte pieces, applied on the copy side by choosing the source
+// piece): half-panel row j keeps source piece q at q ^ 2 sigma(j), sigma(j) =
+// (j & 3) | ((j >> 3) & 1) << 2, so the 32 lanes of a transposing read (8 rows
+// x 32 bytes) cover all 64 banks once; A row r keeps piece q at q ^
+// dt_swa(r), so the 16 rows x 16 bytes of an A read do as well.
+#pragma once
+
+#include "common.h"
+#include "gemm_core.h"
+#include "dma_tile.h"
+
+namespace moe {
+
+constexpr int BD_BM = 256;                         // rows per tile
+constexpr int BD_BN = 256;                         // weight columns per tile
+constexpr int BD_HPROW = 256;                      // bytes per half-panel row (128 columns)
+constexpr int BD_HP = DT_KS * BD_HPROW;            // bytes of one half-panel stage (8 KB)
+constexpr int BD_AOFF = 2 * BD_HP;                 // A rows follow the two half-panels
+constexpr int BD_SLOT = BD_AOFF + BD_BM * DT_KS * 2;  // bytes per ring slot (32 KB)
+#ifndef MOE_BD_NS
+#define MOE_BD_NS 4
+#endif
+constexpr int BD_NS = MOE_BD_NS;                   // ring slots
+constexpr int BD_CNT = 4;                          // copy instructions per wave per stage
+static_assert(BD_NS == 3 || BD_NS == 4, "ring of 3 or 4 slots");
+
+// Per-thread fixed state of the K loop.
+struct BdCtx {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[2];   // A copies a = wave, wave + 8: lane source offsets (bytes) at k 0
+  uint32_t vb;      // weight copy 0: lane source offset at stage row 0; copy 1 reads 4 rows on
+  uint32_t ldb2;    // bytes per row of B
+  int bdst;         // first weight destination of this wave inside a slot
+  int adst;         // first A destination of this wave inside a slot
+  int aoff;         // lane's A fragment offset inside the A region (m-tile 0)
+  int wx;           // lane's weight fragment offset of the wave's n-tile 0
+};
+
+// Stage st into ring slot J.
+template <int J>
+__device__ __forceinline__ void bd_issue(const BdCtx& c, char* ring, int st) {
+  char* slot = ring + J * BD_SLOT;
+  const uint32_t k0 = (uint32_t)(st * DT_KS);
+  const uint32_t sb = k0 * c.ldb2;
+  dt_copy16(c.rb, slot + c.bdst, c.vb, sb);
+  dt_copy16(c.rb, slot + c.bdst + 1024, c.vb, sb + 4 * c.ldb2);
+  dt_copy16(c.ra, slot + c.adst, c.va[0], k0 * 2);
+  dt_copy16(c.ra, slot + c.adst + 8 * 1024, c.va[1], k0 * 2);
+}
+
+// Multiply the stage in slot J.  kleft < DT_KS (last stage only, MASK) zeroes
+// both fragments for k past the end, whatever the slot holds there.
+template <int J, bool MASK, bool SWIGLU>
+__device__ __forceinline__ void bd_compute(const BdCtx& c, const char* ring, int kleft,
+                                           f32x4 (&acc)[4][8]) {
+  const char* slot = ring + J * BD_SLOT;
+  const int g = (threadIdx.x & 63) >> 4;
+  const bool zero = MASK && 8 * g >= kleft;
+  int wx = c.wx;
+  asm volatile("" : "+v"(wx));
+  __builtin_amdgcn_sched_barrier(0);
+  // all fragments of the stage are read first (20 LDS reads in flight), then
+  // the 32 products run back to back, each waiting only for its own operands
+  bf16x8 xf[4], wf[8];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    xf[mt] = *reinterpret_cast<const bf16x8*>(slot + BD_AOFF + c.aoff + 1024 * mt);
+    if (zero) xf[mt] = bf16x8{};
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int off = SWIGLU ? (wx ^ (32 * (t & 3))) + (t >> 2) * BD_HP : wx ^ (32 * t);
+    const s16x4 lo = dt_tr16(slot + off);
+    const s16x4 hi = dt_tr16(slot + off + 4 * BD_HPROW);
+    wf[t] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (zero) wf[t] = bf16x8{};
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma16(wf[t], xf[mt], acc[mt][t]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stage st in slot J = st % BD_NS: wait for it (the newer stages stay in
+// flight), refill the slot of stage st - 1 (every wave is past it) with stage
+// st + BD_NS - 1, multiply.  GUARD: the form with range conditions (tail).
+template <int J, bool GUARD, bool SWIGLU>
+__device__ __forceinline__ void bd_step(const BdCtx& c, char* ring, int st, int nst, int K,
+                                        f32x4 (&acc)[4][8]) {
+  if (GUARD && st >= nst) return;
+  const int ahead = nst - 1 - st;   // stages after st, issued up to BD_NS - 2 of them
+  if (!GUARD || ahead >= BD_NS - 2) dt_sync<(BD_NS - 2) * BD_CNT>();
+  else if (BD_NS == 4 && ahead == 1) dt_sync<BD_CNT>();
+  else dt_sync<0>();
+  if (!GUARD || st + BD_NS - 1 < nst) bd_issue<(J + BD_NS - 1) % BD_NS>(c, ring, st + BD_NS - 1);
+  bd_compute<J, GUARD, SWIGLU>(c, ring, K - st * DT_KS, acc);
+}
+
+template <int J, bool GUARD, bool SWIGLU>
+__device__ __forceinline__ void bd_trip(const BdCtx& c, char* ring, int st, int nst, int K,
+                                        f32x4 (&acc)[4][8]) {
+  bd_step<J, GUARD, SWIGLU>(c, ring, st + J, nst, K, acc);
+  if constexpr (J + 1 < BD_NS) bd_trip<J + 1, GUARD, SWIGLU>(c, ring, st, nst, K, acc);
+}
+
+template <int J>
+__device__ __forceinline__ void bd_prologue(const BdCtx& c, char* ring, int nst) {
+  if constexpr (J < BD_NS - 1) {
+    if (J < nst) bd_issue<J>(c, ring, J);
+    bd_prologue<J + 1>(c, ring, nst);
+  }
+}
+
+// One 256 x 256 tile: rows [r0, r0 + R) (1 <= R <= 256) of A, where A row r is
+// A[r0 + r] or, with a row map, row rows[r0 + r] / rdiv of the abytes-byte
+// matrix A; weight column block nt of expert e.  K and N multiples of 8.
+//   SWIGLU: C[r0 + r][128 nt + h] = rnd(SiLU(A W1) * (A W3)), B1/B3 = [E][K][N]
+//   else:   C[r0 + r][256 nt + n] = rnd(A W2),                 B1 = [E][K][N]
+// ring: BD_NS * BD_SLOT bytes of LDS.  All 512 threads call; the caller
+// separates two tiles of one workgroup with a barrier.
+template <bool SWIGLU>
+__device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
+                                        const bf16_t* __restrict__ B3, int K, int N,
+                                        bf16_t* __restrict__ C, int e, int r0, int R, int nt,
+                                        const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
+                                        char* ring) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t estride = (int64_t)K * N;
+  BdCtx c;
+  // weight copies: half-panel hp = wave >> 2, rows 8 (wave & 3) .. + 7, four
+  // rows (16 lanes each) per instruction; rows j and j + 4 share sigma
+  const int hp = wave >> 2;
+  const bf16_t* Bp = (SWIGLU && hp ? B3 : B1) + e * estride;
+  const int colbase = SWIGLU ? 128 * nt : 256 * nt + 128 * hp;
+  c.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
+  c.ldb2 = (uint32_t)(N * 2);
+  {
+    const int j = 8 * (wave & 3) + (lane >> 4);
+    const int sig = (j & 3) | (((j >> 3) & 1) << 2);
+    const int col = colbase + 8 * ((lane & 15) ^ (2 * sig));
+    c.vb = col < N ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
+  }
+  c.bdst = hp * BD_HP + 2048 * (wave & 3);
+  // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row
+  c.ra = rows ? gc_rsrc(A, abytes) : gc_rsrc(A + (int64_t)r0 * K, (uint32_t)((int64_t)R * K * 2));
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int r = 16 * (wave + 8 * v) + (lane >> 2);
+    const int rr = min(r, R - 1);
+    const uint32_t row = rows ? (uint32_t)(rows[r0 + rr] / rdiv) : (uint32_t)rr;
+    c.va[v] = (row * (uint32_t)K + 8u * (uint32_t)((lane & 3) ^ dt_swa(r))) * 2u;
+  }
+  c.adst = BD_AOFF + 1024 * wave;
+  // fragment reads
+  const int wm = wave & 3, wn = wave >> 2;
+  c.aoff = (64 * wm + i) * 64 + 16 * (g ^ dt_swa(i));
+  // weight fragment of n-tile ti of a half-panel: rows 8 g + i / 4 (and + 4),
+  // columns 16 ti + 4 (i % 4) .. + 3 -> byte row * 256 + (32 (ti ^ sigma) +
+  // 8 (i % 4)), sigma = (i / 4) | (g & 1) << 2; the XOR touches bits 5..7 only
+  const int sig = (i >> 2) | ((g & 1) << 2);
+  const int wlane = (8 * g + (i >> 2)) * BD_HPROW + 32 * sig + 8 * (i & 3);
+  c.wx = SWIGLU ? (wlane ^ (32 * 4 * wn)) : wlane + wn * BD_HP;
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = (K + DT_KS - 1) / DT_KS;
+  if (nst > 0) {
+    bd_prologue<0>(c, ring, nst);
+    int st = 0;
+    for (; st + 2 * BD_NS - 1 <= nst; st += BD_NS) bd_trip<0, false, SWIGLU>(c, ring, st, nst, K, acc);
+    bd_trip<0, true, SWIGLU>(c, ring, st, nst, K, acc);
+    bd_trip<0, true, SWIGLU>(c, ring, st + BD_NS, nst, K, acc);
+  }
+
+  // epilogue: lane (i, g), m-tile mt, n-tile t holds row 64 wm + 16 mt + i,
+  // weight columns 16 t + 4 g .. + 3 of the wave's n-tile range
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = 64 * wm + 16 * mt + i;
+#pragma unroll
+    for (int t = 0; t < (SWIGLU ? 4 : 8); ++t) {
+      const int col = SWIGLU ? 128 * nt + 64 * wn + 16 * t + 4 * g : 256 * nt + 128 * wn + 16 * t + 4 * g;
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = acc[mt][t][r];
+        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a;
+      }
+      if (row < R && col < N)
+        *reinterpret_cast<u32x2*>(C + (int64_t)(r0 + row) * N + col) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+}  // namespace moe

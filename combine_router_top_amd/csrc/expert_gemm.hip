@@ -36,8 +36,8 @@
 #include "common.h"
 #include "kernels.h"
 #include "gemm_core.h"
-#include "lds_tile.h"
 #include "dma_tile.h"
+#include "dma_big.h"
 
 namespace moe {
 
@@ -282,18 +282,12 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
 // ---------------------------------------------------------------------------
 // For experts with at least XB_TH rows the weight-streaming kernel above would
 // re-read the weights once per 160-row block; here a workgroup of 8 waves
-// computes a 256-row x 256-weight-column tile, each wave 128 x 64
-// (accumulators in AGPRs, two waves per SIMD).  Per 64-K stage every thread
-// loads 4 A vectors and one 8 x 4 weight block with buffer loads (fixed lane
-// offsets, scalar stage offsets); the next stage is in flight while the
-// current one is multiplied; the weight block is transposed in registers and
-// both are written into the other LDS buffer.  Weight columns are placed in
-// LDS so that each lane's 4 n-tiles are 4 consecutive output columns (8-byte
-// stores), and for GEMM-1 so that W1 and W3 of one column meet in lanes i and
-// i ^ 8.  The lower four waves load W1 blocks, the upper four W3 blocks, so
-// every buffer descriptor is wave-uniform.
-constexpr int XB_BM = 256;
-constexpr int XB_BN = XT_BN;    // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
+// computes a 256-row x 256-weight-column tile (dma_big.h: both operands
+// copied from memory straight into a ring of LDS slots, three 32-K stages in
+// flight, weights read with transposing LDS reads, each wave 64 rows x 128
+// weight columns, two waves per SIMD).
+constexpr int XB_BM = BD_BM;
+constexpr int XB_BN = BD_BN;    // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
 constexpr int XB_NW = 8;        // waves per workgroup
 #ifndef MOE_XB_TH
 #define MOE_XB_TH 320
@@ -358,68 +352,6 @@ __device__ BigTile big_tile_at(int L, const int32_t* __restrict__ offsets, int e
   return bt;
 }
 
-struct BigRegs {
-  u32x4 a[4];
-  u32x2 b[8];
-};
-
-// Per-thread fixed state of the large-tile loop: buffer descriptors (wave
-// uniform) and byte offsets that do not change with K.
-struct BigCtx {
-  __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[4];   // A rows (t >> 3) + 64 j, 16-byte chunk t & 7
-  uint32_t vb;      // B block: k rows 8 kb .. 8 kb + 7 (via scalar offsets), 4 columns
-  uint32_t ldb2;    // B row bytes
-  int kb, nb;       // block coordinates inside the 64 x 256 weight stage (nb: 4-column group)
-};
-
-__device__ __forceinline__ void big_issue(BigRegs& R, const BigCtx& c, int k0) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    R.a[j] = __builtin_amdgcn_raw_buffer_load_b128(c.ra, c.va[j], (uint32_t)(k0 * 2), 0);
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-    R.b[r] = __builtin_amdgcn_raw_buffer_load_b64(c.rb, c.vb, (uint32_t)(k0 + r) * c.ldb2, 0);
-}
-
-template <bool SWIGLU>
-__device__ __forceinline__ void big_store(const BigRegs& R, const BigCtx& c, bf16_t* As, bf16_t* Bs) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *reinterpret_cast<u32x4*>(As + ((t >> 3) + 64 * j) * GC_LDA + 8 * (t & 7)) = R.a[j];
-#pragma unroll
-  for (int col = 0; col < 4; ++col) {
-    const uint32_t sel = (col & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 v;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      v[q] = __builtin_amdgcn_perm(R.b[2 * q + 1][col >> 1], R.b[2 * q][col >> 1], sel);
-    *reinterpret_cast<u32x4*>(Bs + tile_brow<SWIGLU>(c.nb, col) * GC_LDA + 8 * c.kb) = v;
-  }
-}
-
-__device__ __forceinline__ void big_compute(const bf16_t* As, const bf16_t* Bs, int wm, int wn,
-                                            f32x4 (&acc)[8][4]) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, g = lane >> 4;
-  const bf16_t* a0 = As + (128 * wm + i) * GC_LDA + 8 * g;
-  const bf16_t* b0 = Bs + (64 * wn + i) * GC_LDA + 8 * g;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    bf16x8 bf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      bf[t] = *reinterpret_cast<const bf16x8*>(b0 + 16 * t * GC_LDA + 32 * sub);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(a0 + 16 * mt * GC_LDA + 32 * sub);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = mfma16(af, bf[t], acc[mt][t]);
-    }
-  }
-}
-
 static_assert(XGThin::NW == 8 && XB_NW == 8, "one workgroup size for all streamed tile classes");
 // The thin tiles borrow the medium ring slots: the A stages in slot 0, the
 // W3 -> W1 accumulator exchange in slots 1 and 2 (half of the pairs each).
@@ -478,94 +410,6 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
 // SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
 // K and N tails are bounded by the buffer descriptors.
-template <bool SWIGLU>
-__device__ __forceinline__ void big_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
-                                         const bf16_t* __restrict__ B3, int K, int N,
-                                         bf16_t* __restrict__ C, const BigTile& bt, const RowMap& rm,
-                                         bf16_t (*As)[XB_BM * GC_LDA], bf16_t (*Bs)[XB_BN * GC_LDA]) {
-  const int t = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t estride = (int64_t)K * N;
-  BigCtx c;
-  const bf16_t* Bp;
-  int bcol;
-  if (SWIGLU) {  // waves 0-3 load W1 blocks, waves 4-7 the same W3 blocks
-    const int u = t & 255;
-    c.kb = u >> 5;
-    c.nb = (u & 31) + (wave >= 4 ? 32 : 0);
-    Bp = (wave < 4 ? B1 : B3) + bt.e * estride;
-    bcol = bt.nt * 128 + 4 * (u & 31);
-  } else {
-    c.kb = t >> 6;
-    c.nb = t & 63;
-    Bp = B1 + bt.e * estride;
-    bcol = bt.nt * 256 + 4 * c.nb;
-  }
-  c.ra = rm.rows ? gc_rsrc(A, rm.bytes)
-                 : gc_rsrc(A + (int64_t)bt.r0 * K, (uint32_t)((int64_t)bt.R * K * 2));
-  c.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = min((t >> 3) + 64 * j, bt.R - 1);
-    const int64_t row = rm.rows ? (int64_t)(rm.rows[bt.r0 + r] / rm.div) : (int64_t)r;
-    c.va[j] = (uint32_t)((row * K + 8 * (t & 7)) * 2);
-  }
-  c.vb = bcol < N ? (uint32_t)(((int64_t)(8 * c.kb) * N + bcol) * 2) : GC_OOR;
-  c.ldb2 = (uint32_t)(N * 2);
-
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nst = (K + GC_KS - 1) / GC_KS;
-  BigRegs R;
-  big_issue(R, c, 0);
-  big_store<SWIGLU>(R, c, As[0], Bs[0]);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) big_issue(R, c, (st + 1) * GC_KS);
-    __builtin_amdgcn_sched_barrier(0);
-    big_compute(As[cur], Bs[cur], wm, wn, acc);
-    if (st + 1 < nst) big_store<SWIGLU>(R, c, As[cur ^ 1], Bs[cur ^ 1]);
-    __syncthreads();
-  }
-  // epilogue: lane (i, g) of wave (wm, wn) holds, for n-tile q, rows
-  // 128 wm + 16 mt + 4 g + r of output column base + 4 (i or i & 7) + q
-  const int lane = t & 63;
-  const int i = lane & 15, g = lane >> 4;
-  int ocol;
-  if (SWIGLU) ocol = bt.nt * 128 + 32 * wn + 4 * (i & 7);
-  else ocol = bt.nt * 256 + 64 * wn + 4 * i;
-  const bool store_lane = (SWIGLU ? (i < 8) : true) && ocol < N;
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = acc[mt][q][r];
-        if (SWIGLU) {
-          const float b = __shfl_xor(a, 8);
-          o[q] = a / (1.0f + expf(-a)) * b;
-        } else {
-          o[q] = a;
-        }
-      }
-      const int row = 128 * wm + 16 * mt + 4 * g + r;
-      if (store_lane && row < bt.R)
-        *reinterpret_cast<u32x2*>(C + (int64_t)(bt.r0 + row) * N + ocol) =
-            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
-  }
-}
-
-// SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
-// else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
-// K and N tails are bounded by the buffer descriptors.
 //
 // The tile order is cut into 8 contiguous ranges, one per XCD (workgroup id
 // mod 8 on this part); workgroup (x, q) of the G = gridDim.x takes tiles
@@ -578,8 +422,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets, int e_begin, int e_end,
     const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3, int K, int N,
     bf16_t* __restrict__ C, int ntn, RowMap rm) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
+  __shared__ __attribute__((aligned(16))) char ring[BD_NS * BD_SLOT];
   __shared__ int pre[XG_MAXN + 1];
   const int ne = e_end - e_begin;
   const int tot_m = big_prefix(offsets, e_begin, ne, pre);
@@ -597,13 +440,20 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     end = TT;
     step = G;
   }
-  for (; L < end; L += step) {
+  for (bool first = true; L < end; L += step, first = false) {
     BigTile bt = big_tile_at(L, offsets, e_begin, ne, ntn, tot_m, pre);
     bt.e = __builtin_amdgcn_readfirstlane(bt.e);
     bt.r0 = __builtin_amdgcn_readfirstlane(bt.r0);
     bt.R = __builtin_amdgcn_readfirstlane(bt.R);
     bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
-    big_tile<SWIGLU>(A, B1, B3, K, N, C, bt, rm, As, Bs);
+    // a later tile refills the ring: every wave must be done with the
+    // previous one, and its epilogue stores retired (loads and stores share
+    // the counter that the ring's waits count)
+    if (!first) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    bd_tile<SWIGLU>(A, B1, B3, K, N, C, bt.e, bt.r0, bt.R, bt.nt, rm.rows, rm.div, rm.bytes, ring);
   }
 }
 
@@ -622,8 +472,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
 __global__ __launch_bounds__(64 * XB_NW, 1) void gemm_signal_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C, int M,
     int N, int K, int ntn, uint32_t* __restrict__ flags, uint32_t epoch, int system_scope) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][XB_BM * GC_LDA];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][XB_BN * GC_LDA];
+  __shared__ __attribute__((aligned(16))) char ring[BD_NS * BD_SLOT];
   const int tile = blockIdx.x;
   const int tm = tile / ntn;
   BigTile bt;
@@ -631,7 +480,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void gemm_signal_kernel(
   bt.r0 = tm * XB_BM;
   bt.R = min(XB_BM, M - bt.r0);
   bt.nt = tile - tm * ntn;
-  big_tile<false>(A, B, nullptr, K, N, C, bt, RowMap{nullptr, 1, 0}, As, Bs);
+  bd_tile<false>(A, B, nullptr, K, N, C, 0, bt.r0, bt.R, bt.nt, nullptr, 1, 0, ring);
   // every thread's stores of the tile complete and visible at the scope,
   // then one release store of the flag
   if (system_scope) __threadfence_system();
