@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense flop/s
 METRIC = "MoE layer tokens/s on 1 MI355X; grouped-GEMM % MFMA peak, dispatch % HBM"
-GEMM_SOURCES = ["expert_gemm.hip", "dma_tile.h", "lds_tile.h", "gemm_core.h", "mfma_tile.h", "common.h"]
+GEMM_SOURCES = ["expert_gemm.hip", "dma_tile.h", "dma_big.h", "gemm_core.h", "mfma_tile.h", "common.h"]
 
 
 def parse():

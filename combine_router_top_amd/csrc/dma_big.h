@@ -10,10 +10,14 @@
 // 32 K of all 256 A rows, each wave with two weight and two A copy
 // instructions of 16 bytes per lane (weight copies read four 256-byte row
 // runs, A copies sixteen 64-byte runs).  No register holds the data in transit
-// and no instruction rewrites it.  The ring has BD_NS slots of 32 KB, so
-// BD_NS - 1 stages are in flight while one is multiplied; a stage is released
-// by an explicit wait for the wave's own copies and one barrier (the
-// copy/wait/barrier protocol of dma_tile.h).
+// and no instruction rewrites it.  The ring has BD_NS slots of 32 KB and a
+// wave holds the fragments of the stage it multiplies in registers, so
+// BD_NS - 1 stages are in flight; a stage is released by an explicit wait for
+// the wave's own copies and one barrier (the copy/wait/barrier protocol of
+// dma_tile.h).  Four slots measured as fast as five (all of LDS); the tile is
+// bound by the rate at which a compute unit's copies complete (each spans 8 to
+// 16 cache lines, and about one line in six misses L2), not by the matrix
+// cores.
 //
 // Wave w = (wm, wn) = (w & 3, w >> 2) multiplies rows 64 wm .. 64 wm + 63 by
 // 128 weight columns: GEMM-1 h columns 64 wn .. 64 wn + 63 of W1 (n-tiles
@@ -48,7 +52,10 @@ constexpr int BD_SLOT = BD_AOFF + BD_BM * DT_KS * 2;  // bytes per ring slot (32
 #endif
 constexpr int BD_NS = MOE_BD_NS;                   // ring slots
 constexpr int BD_CNT = 4;                          // copy instructions per wave per stage
-static_assert(BD_NS == 3 || BD_NS == 4, "ring of 3 or 4 slots");
+static_assert(BD_NS == 4 || BD_NS == 5, "ring of 4 or 5 slots");
+// steps per unrolled trip: fragments alternate between two register sets, so
+// a trip returns to the first set after an even number of steps
+constexpr int BD_TL = BD_NS % 2 ? 2 * BD_NS : BD_NS;
 
 // Per-thread fixed state of the K loop.
 struct BdCtx {
@@ -60,82 +67,137 @@ struct BdCtx {
   int adst;         // first A destination of this wave inside a slot
   int aoff;         // lane's A fragment offset inside the A region (m-tile 0)
   int wx;           // lane's weight fragment offset of the wave's n-tile 0
+  uint32_t lbase;   // LDS address of the ring
 };
+
+// 16 bytes per lane from the buffer into LDS at byte address lds + 16 lane of
+// the LDS aperture (lds wave-uniform); as dt_copy16, but with a 32-bit LDS
+// address, so that no generic pointer per destination is kept in registers.
+__device__ __forceinline__ void bd_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
+                                          uint32_t soff) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+      : "memory");
+}
 
 // Stage st into ring slot J.
 template <int J>
-__device__ __forceinline__ void bd_issue(const BdCtx& c, char* ring, int st) {
-  char* slot = ring + J * BD_SLOT;
+__device__ __forceinline__ void bd_issue(const BdCtx& c, int st) {
+  // recomputed per stage from one base, so that the unrolled loop does not
+  // keep an address per slot and copy in scalar registers
+  uint32_t b = c.lbase;
+  asm volatile("" : "+s"(b));
+  const uint32_t slot = b + (uint32_t)(J * BD_SLOT);
   const uint32_t k0 = (uint32_t)(st * DT_KS);
   const uint32_t sb = k0 * c.ldb2;
-  dt_copy16(c.rb, slot + c.bdst, c.vb, sb);
-  dt_copy16(c.rb, slot + c.bdst + 1024, c.vb, sb + 4 * c.ldb2);
-  dt_copy16(c.ra, slot + c.adst, c.va[0], k0 * 2);
-  dt_copy16(c.ra, slot + c.adst + 8 * 1024, c.va[1], k0 * 2);
+  bd_copy16(c.rb, slot + c.bdst, c.vb, sb);
+  bd_copy16(c.rb, slot + c.bdst + 1024, c.vb, sb + 4 * c.ldb2);
+  bd_copy16(c.ra, slot + c.adst, c.va[0], k0 * 2);
+  bd_copy16(c.ra, slot + c.adst + 8 * 1024, c.va[1], k0 * 2);
 }
 
-// Multiply the stage in slot J.  kleft < DT_KS (last stage only, MASK) zeroes
-// both fragments for k past the end, whatever the slot holds there.
-template <int J, bool MASK, bool SWIGLU>
-__device__ __forceinline__ void bd_compute(const BdCtx& c, const char* ring, int kleft,
-                                           f32x4 (&acc)[4][8]) {
+// The fragments of one stage: 4 A fragments (m-tiles) and 8 weight fragments
+// (n-tiles).
+struct BdFrag {
+  bf16x8 x[4], w[8];
+};
+
+// Reads of the stage in slot J: the A fragments, and the weight fragment of
+// n-tile t.  kleft < DT_KS (last stage only, MASK) zeroes both fragments for
+// k past the end, whatever the slot holds there.
+template <int J, bool MASK>
+__device__ __forceinline__ void bd_read_x(const BdCtx& c, const char* ring, int kleft, BdFrag& f) {
   const char* slot = ring + J * BD_SLOT;
-  const int g = (threadIdx.x & 63) >> 4;
-  const bool zero = MASK && 8 * g >= kleft;
-  int wx = c.wx;
-  asm volatile("" : "+v"(wx));
-  __builtin_amdgcn_sched_barrier(0);
-  // all fragments of the stage are read first (20 LDS reads in flight), then
-  // the 32 products run back to back, each waiting only for its own operands
-  bf16x8 xf[4], wf[8];
+  const bool zero = MASK && 8 * ((threadIdx.x & 63) >> 4) >= kleft;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    xf[mt] = *reinterpret_cast<const bf16x8*>(slot + BD_AOFF + c.aoff + 1024 * mt);
-    if (zero) xf[mt] = bf16x8{};
+    f.x[mt] = *reinterpret_cast<const bf16x8*>(slot + BD_AOFF + c.aoff + 1024 * mt);
+    if (zero) f.x[mt] = bf16x8{};
   }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int off = SWIGLU ? (wx ^ (32 * (t & 3))) + (t >> 2) * BD_HP : wx ^ (32 * t);
-    const s16x4 lo = dt_tr16(slot + off);
-    const s16x4 hi = dt_tr16(slot + off + 4 * BD_HPROW);
-    wf[t] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    if (zero) wf[t] = bf16x8{};
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma16(wf[t], xf[mt], acc[mt][t]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
-  __builtin_amdgcn_sched_barrier(0);
+}
+template <int J, bool MASK, bool SWIGLU>
+__device__ __forceinline__ void bd_read_w(const char* ring, int wx, int t, int kleft, BdFrag& f) {
+  const char* slot = ring + J * BD_SLOT;
+  const bool zero = MASK && 8 * ((threadIdx.x & 63) >> 4) >= kleft;
+  const int off = SWIGLU ? (wx ^ (32 * (t & 3))) + (t >> 2) * BD_HP : wx ^ (32 * t);
+  const s16x4 lo = dt_tr16(slot + off);
+  const s16x4 hi = dt_tr16(slot + off + 4 * BD_HPROW);
+  f.w[t] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  if (zero) f.w[t] = bf16x8{};
 }
 
-// Stage st in slot J = st % BD_NS: wait for it (the newer stages stay in
-// flight), refill the slot of stage st - 1 (every wave is past it) with stage
-// st + BD_NS - 1, multiply.  GUARD: the form with range conditions (tail).
+// Wait until at most N of this wave's copies are outstanding and its LDS
+// reads have completed (so that the slot they read may be refilled), then
+// barrier.
+template <int N>
+__device__ __forceinline__ void bd_sync() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// bd_sync with n (0..4) newer stages left in flight (n wave-uniform).
+__device__ __forceinline__ void bd_sync_n(int n) {
+  if (n >= 4) bd_sync<4 * BD_CNT>();
+  else if (n == 3) bd_sync<3 * BD_CNT>();
+  else if (n == 2) bd_sync<2 * BD_CNT>();
+  else if (n == 1) bd_sync<BD_CNT>();
+  else bd_sync<0>();
+}
+
+// Step st (slot J = st % BD_NS), F holding stage st's fragments: wait for
+// stage st + 1 and barrier (every wave then holds stage st in registers, so
+// slot J is free), refill slot J with stage st + BD_NS, then read stage st + 1
+// into G while multiplying F.  GUARD: the form with range conditions (tail).
 template <int J, bool GUARD, bool SWIGLU>
 __device__ __forceinline__ void bd_step(const BdCtx& c, char* ring, int st, int nst, int K,
-                                        f32x4 (&acc)[4][8]) {
+                                        BdFrag& F, BdFrag& G, f32x4 (&acc)[4][8]) {
   if (GUARD && st >= nst) return;
-  const int ahead = nst - 1 - st;   // stages after st, issued up to BD_NS - 2 of them
-  if (!GUARD || ahead >= BD_NS - 2) dt_sync<(BD_NS - 2) * BD_CNT>();
-  else if (BD_NS == 4 && ahead == 1) dt_sync<BD_CNT>();
-  else dt_sync<0>();
-  if (!GUARD || st + BD_NS - 1 < nst) bd_issue<(J + BD_NS - 1) % BD_NS>(c, ring, st + BD_NS - 1);
-  bd_compute<J, GUARD, SWIGLU>(c, ring, K - st * DT_KS, acc);
+  const bool next = !GUARD || st + 1 < nst;
+  if (next) {
+    // issued stages after st + 1: BD_NS - 2, fewer near the end
+    if (!GUARD) bd_sync<(BD_NS - 2) * BD_CNT>();
+    else bd_sync_n(min(nst - 2 - st, BD_NS - 2));
+    if (!GUARD || st + BD_NS < nst) bd_issue<J % BD_NS>(c, st + BD_NS);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // stage st + 1's A fragments, then per n-tile t: the 4 products of F's
+  // fragment t and the reads of G's fragment t, which can take its registers
+  const int kl = K - (st + 1) * DT_KS;
+  int wx = c.wx;
+  asm volatile("" : "+v"(wx));
+  if (next) bd_read_x<(J + 1) % BD_NS, GUARD>(c, ring, kl, G);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma16(F.w[t], F.x[mt], acc[mt][t]);
+    if (next) bd_read_w<(J + 1) % BD_NS, GUARD, SWIGLU>(ring, wx, t, kl, G);
+  }
+  if (next) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int J, bool GUARD, bool SWIGLU>
 __device__ __forceinline__ void bd_trip(const BdCtx& c, char* ring, int st, int nst, int K,
-                                        f32x4 (&acc)[4][8]) {
-  bd_step<J, GUARD, SWIGLU>(c, ring, st + J, nst, K, acc);
-  if constexpr (J + 1 < BD_NS) bd_trip<J + 1, GUARD, SWIGLU>(c, ring, st, nst, K, acc);
+                                        BdFrag& F, BdFrag& G, f32x4 (&acc)[4][8]) {
+  // fragments alternate between F and G from step to step
+  bd_step<J, GUARD, SWIGLU>(c, ring, st + J, nst, K, F, G, acc);
+  if constexpr (J + 1 < BD_TL) bd_trip<J + 1, GUARD, SWIGLU>(c, ring, st, nst, K, G, F, acc);
 }
 
 template <int J>
 __device__ __forceinline__ void bd_prologue(const BdCtx& c, char* ring, int nst) {
-  if constexpr (J < BD_NS - 1) {
-    if (J < nst) bd_issue<J>(c, ring, J);
+  if constexpr (J < BD_NS) {
+    if (J < nst) bd_issue<J>(c, J);
     bd_prologue<J + 1>(c, ring, nst);
   }
 }
@@ -172,6 +234,7 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
     c.vb = col < N ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
   }
   c.bdst = hp * BD_HP + 2048 * (wave & 3);
+  c.lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dt_lds_t*)ring);
   // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row
   c.ra = rows ? gc_rsrc(A, abytes) : gc_rsrc(A + (int64_t)r0 * K, (uint32_t)((int64_t)R * K * 2));
 #pragma unroll
@@ -199,11 +262,17 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
     for (int t = 0; t < 8; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nst = (K + DT_KS - 1) / DT_KS;
   if (nst > 0) {
-    bd_prologue<0>(c, ring, nst);
+    bd_prologue<0>(c, ring, nst);   // stages 0 .. BD_NS - 1 into every slot
+    bd_sync_n(min(nst - 1, BD_NS - 1));
+    BdFrag F, G;
+    bd_read_x<0, true>(c, ring, K, F);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) bd_read_w<0, true, SWIGLU>(ring, c.wx, t, K, F);
     int st = 0;
-    for (; st + 2 * BD_NS - 1 <= nst; st += BD_NS) bd_trip<0, false, SWIGLU>(c, ring, st, nst, K, acc);
-    bd_trip<0, true, SWIGLU>(c, ring, st, nst, K, acc);
-    bd_trip<0, true, SWIGLU>(c, ring, st + BD_NS, nst, K, acc);
+    // an unguarded trip issues up to stage st + BD_TL - 1 + BD_NS
+    for (; st + BD_TL + BD_NS <= nst; st += BD_TL) bd_trip<0, false, SWIGLU>(c, ring, st, nst, K, F, G, acc);
+    bd_trip<0, true, SWIGLU>(c, ring, st, nst, K, F, G, acc);
+    bd_trip<0, true, SWIGLU>(c, ring, st + BD_TL, nst, K, F, G, acc);
   }
 
   // epilogue: lane (i, g), m-tile mt, n-tile t holds row 64 wm + 16 mt + i,

@@ -423,7 +423,9 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3, int K, int N,
     bf16_t* __restrict__ C, int ntn, RowMap rm) {
   __shared__ __attribute__((aligned(16))) char ring[BD_NS * BD_SLOT];
-  __shared__ int pre[XG_MAXN + 1];
+  // the tile table lives in the ring until a tile's K loop starts
+  static_assert((XG_MAXN + 1) * 4 <= BD_NS * BD_SLOT, "tile table fits the ring");
+  int* pre = reinterpret_cast<int*>(ring);
   const int ne = e_end - e_begin;
   const int tot_m = big_prefix(offsets, e_begin, ne, pre);
   const int TT = tot_m * ntn;
@@ -441,18 +443,20 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     step = G;
   }
   for (bool first = true; L < end; L += step, first = false) {
+    if (!first) {
+      // the previous tile's K loop overwrote the table: every wave must be
+      // done with the ring and its epilogue stores retired (loads and stores
+      // share the counter that the ring's waits count) before it is rebuilt
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      big_prefix(offsets, e_begin, ne, pre);
+    }
     BigTile bt = big_tile_at(L, offsets, e_begin, ne, ntn, tot_m, pre);
     bt.e = __builtin_amdgcn_readfirstlane(bt.e);
     bt.r0 = __builtin_amdgcn_readfirstlane(bt.r0);
     bt.R = __builtin_amdgcn_readfirstlane(bt.R);
     bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
-    // a later tile refills the ring: every wave must be done with the
-    // previous one, and its epilogue stores retired (loads and stores share
-    // the counter that the ring's waits count)
-    if (!first) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
+    __syncthreads();   // every wave has read the table before the copies overwrite it
     bd_tile<SWIGLU>(A, B1, B3, K, N, C, bt.e, bt.r0, bt.R, bt.nt, rm.rows, rm.div, rm.bytes, ring);
   }
 }
