@@ -477,13 +477,25 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void gemm_signal_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C, int M,
     int N, int K, int ntn, uint32_t* __restrict__ flags, uint32_t epoch, int system_scope) {
   __shared__ __attribute__((aligned(16))) char ring[BD_NS * BD_SLOT];
-  const int tile = blockIdx.x;
-  const int tm = tile / ntn;
+  // Workgroup -> tile as in the grouped kernel: the G = gridDim.x tiles (one
+  // workgroup each) are cut into 8 ranges, one per XCD (workgroup id mod 8),
+  // and inside a range tiles run in groups of XB_GM m-tiles, m fastest, so
+  // the tiles an XCD has in flight share A and B panels in its L2.  The flag
+  // and the output keep the row-major tile number tm * ntn + tn.
+  const int G = gridDim.x;
+  const int L = (G & 7) == 0 ? (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int ntm = G / ntn;
+  const int mg = L / (XB_GM * ntn);
+  const int rem = L - mg * XB_GM * ntn;
+  const int gsz = min(XB_GM, ntm - mg * XB_GM);
+  const int tn = rem / gsz;
+  const int tm = mg * XB_GM + (rem - tn * gsz);
+  const int tile = tm * ntn + tn;
   BigTile bt;
   bt.e = 0;
   bt.r0 = tm * XB_BM;
   bt.R = min(XB_BM, M - bt.r0);
-  bt.nt = tile - tm * ntn;
+  bt.nt = tn;
   bd_tile<false>(A, B, nullptr, K, N, C, 0, bt.r0, bt.R, bt.nt, nullptr, 1, 0, ring);
   // every thread's stores of the tile complete and visible at the scope,
   // then one release store of the flag
