@@ -202,30 +202,40 @@ __device__ __forceinline__ void bd_prologue(const BdCtx& c, char* ring, int nst)
   }
 }
 
-// One 256 x 256 tile: rows [r0, r0 + R) (1 <= R <= 256) of A, where A row r is
-// A[r0 + r] or, with a row map, row rows[r0 + r] / rdiv of the abytes-byte
-// matrix A; weight column block nt of expert e.  K and N multiples of 8.
-//   SWIGLU: C[r0 + r][128 nt + h] = rnd(SiLU(A W1) * (A W3)), B1/B3 = [E][K][N]
-//   else:   C[r0 + r][256 nt + n] = rnd(A W2),                 B1 = [E][K][N]
-// ring: BD_NS * BD_SLOT bytes of LDS.  All 512 threads call; the caller
-// separates two tiles of one workgroup with a barrier.
+// K loop of one 256 x 256 tile: acc = A[rows, 0 : klen] . B[0 : klen, cols],
+// where A row r is A[(r0 + r) lda + k] or, with a row map, row rows[r0 + r] /
+// rdiv of the abytes-byte matrix A (row stride lda), and B is row-major with
+// N columns (row 0 = k 0) and brows readable rows; klen <= brows.  Columns:
+// weight column block nt (GEMM-1: 128 columns of B1 and the same of B3).
+// Rows past R, k past klen and columns past N read zeros or meet zeros.
+// lda, N multiples of 8.  ring: BD_NS * BD_SLOT bytes of LDS.  All 512
+// threads call; the caller separates two tiles of one workgroup with a barrier.
+// acc[mt][t] of lane (i, g) of wave (wm, wn) = (w & 3, w >> 2): row
+// 64 wm + 16 mt + i, weight columns 16 t + 4 g .. + 3 of the wave's range
+// (GEMM-1: h columns 128 nt + 64 wn + 16 (t & 3) + 4 g, of W1 for t < 4 and of
+// W3 for t >= 4; otherwise columns 256 nt + 128 wn + 16 t + 4 g).
 template <bool SWIGLU>
-__device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
-                                        const bf16_t* __restrict__ B3, int K, int N,
-                                        bf16_t* __restrict__ C, int e, int r0, int R, int nt,
-                                        const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
-                                        char* ring) {
+__device__ __forceinline__ void bd_accum(const bf16_t* __restrict__ A, int64_t lda,
+                                         const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3,
+                                         int64_t brows, int klen, int N, int r0, int R, int nt,
+                                         const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
+                                         char* ring, f32x4 (&acc)[4][8]) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t estride = (int64_t)K * N;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = (klen + DT_KS - 1) / DT_KS;
+  if (nst <= 0) return;
   BdCtx c;
   // weight copies: half-panel hp = wave >> 2, rows 8 (wave & 3) .. + 7, four
   // rows (16 lanes each) per instruction; rows j and j + 4 share sigma
   const int hp = wave >> 2;
-  const bf16_t* Bp = (SWIGLU && hp ? B3 : B1) + e * estride;
+  const bf16_t* Bp = SWIGLU && hp ? B3 : B1;
   const int colbase = SWIGLU ? 128 * nt : 256 * nt + 128 * hp;
-  c.rb = gc_rsrc(Bp, (uint32_t)(estride * 2));
+  c.rb = gc_rsrc(Bp, (uint32_t)(brows * N * 2));
   c.ldb2 = (uint32_t)(N * 2);
   {
     const int j = 8 * (wave & 3) + (lane >> 4);
@@ -235,14 +245,17 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
   }
   c.bdst = hp * BD_HP + 2048 * (wave & 3);
   c.lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dt_lds_t*)ring);
-  // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row
-  c.ra = rows ? gc_rsrc(A, abytes) : gc_rsrc(A + (int64_t)r0 * K, (uint32_t)((int64_t)R * K * 2));
+  // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row.
+  // Without a row map the descriptor ends at the block's last element, k = klen
+  // of row R - 1 (A may start inside a row: a K range of a wider matrix)
+  c.ra = rows ? gc_rsrc(A, abytes)
+              : gc_rsrc(A + (int64_t)r0 * lda, (uint32_t)(((int64_t)(R - 1) * lda + klen) * 2));
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     const int r = 16 * (wave + 8 * v) + (lane >> 2);
     const int rr = min(r, R - 1);
     const uint32_t row = rows ? (uint32_t)(rows[r0 + rr] / rdiv) : (uint32_t)rr;
-    c.va[v] = (row * (uint32_t)K + 8u * (uint32_t)((lane & 3) ^ dt_swa(r))) * 2u;
+    c.va[v] = (row * (uint32_t)lda + 8u * (uint32_t)((lane & 3) ^ dt_swa(r))) * 2u;
   }
   c.adst = BD_AOFF + 1024 * wave;
   // fragment reads
@@ -255,28 +268,38 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
   const int wlane = (8 * g + (i >> 2)) * BD_HPROW + 32 * sig + 8 * (i & 3);
   c.wx = SWIGLU ? (wlane ^ (32 * 4 * wn)) : wlane + wn * BD_HP;
 
-  f32x4 acc[4][8];
+  bd_prologue<0>(c, ring, nst);   // stages 0 .. BD_NS - 1 into every slot
+  bd_sync_n(min(nst - 1, BD_NS - 1));
+  BdFrag F, G;
+  bd_read_x<0, true>(c, ring, klen, F);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nst = (K + DT_KS - 1) / DT_KS;
-  if (nst > 0) {
-    bd_prologue<0>(c, ring, nst);   // stages 0 .. BD_NS - 1 into every slot
-    bd_sync_n(min(nst - 1, BD_NS - 1));
-    BdFrag F, G;
-    bd_read_x<0, true>(c, ring, K, F);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) bd_read_w<0, true, SWIGLU>(ring, c.wx, t, K, F);
-    int st = 0;
-    // an unguarded trip issues up to stage st + BD_TL - 1 + BD_NS
-    for (; st + BD_TL + BD_NS <= nst; st += BD_TL) bd_trip<0, false, SWIGLU>(c, ring, st, nst, K, F, G, acc);
-    bd_trip<0, true, SWIGLU>(c, ring, st, nst, K, F, G, acc);
-    bd_trip<0, true, SWIGLU>(c, ring, st + BD_TL, nst, K, F, G, acc);
-  }
+  for (int t = 0; t < 8; ++t) bd_read_w<0, true, SWIGLU>(ring, c.wx, t, klen, F);
+  int st = 0;
+  // an unguarded trip issues up to stage st + BD_TL - 1 + BD_NS
+  for (; st + BD_TL + BD_NS <= nst; st += BD_TL) bd_trip<0, false, SWIGLU>(c, ring, st, nst, klen, F, G, acc);
+  bd_trip<0, true, SWIGLU>(c, ring, st, nst, klen, F, G, acc);
+  bd_trip<0, true, SWIGLU>(c, ring, st + BD_TL, nst, klen, F, G, acc);
+}
 
-  // epilogue: lane (i, g), m-tile mt, n-tile t holds row 64 wm + 16 mt + i,
-  // weight columns 16 t + 4 g .. + 3 of the wave's n-tile range
+// One 256 x 256 tile: rows [r0, r0 + R) (1 <= R <= 256) of A, where A row r is
+// A[r0 + r] or, with a row map, row rows[r0 + r] / rdiv of the abytes-byte
+// matrix A; weight column block nt of expert e.  K and N multiples of 8.
+//   SWIGLU: C[r0 + r][128 nt + h] = rnd(SiLU(A W1) * (A W3)), B1/B3 = [E][K][N]
+//   else:   C[r0 + r][256 nt + n] = rnd(A W2),                 B1 = [E][K][N]
+template <bool SWIGLU>
+__device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
+                                        const bf16_t* __restrict__ B3, int K, int N,
+                                        bf16_t* __restrict__ C, int e, int r0, int R, int nt,
+                                        const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
+                                        char* ring) {
+  const int64_t estride = (int64_t)K * N;
+  f32x4 acc[4][8];
+  bd_accum<SWIGLU>(A, K, B1 + e * estride, SWIGLU ? B3 + e * estride : nullptr, K, K, N, r0, R, nt,
+                   rows, rdiv, abytes, ring, acc);
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int row = 64 * wm + 16 * mt + i;

@@ -50,6 +50,11 @@ SMALL = {
     # column-weighted XCD split
     "narrow_mcols_down": W("narrow_mcols_down", 480, 7168, 16, 2, 128, 0, 16, "bf16", seed=17),
     "narrow_mcols_up": W("narrow_mcols_up", 480, 128, 16, 2, 3072, 0, 16, "bf16", seed=18),
+    # wide router with two token blocks and four K splits (the last one 72
+    # deep, a K tail), 40 experts inside a 256-column block
+    "wide_ksplit": W("wide_ksplit", 300, 1032, 40, 4, 64, 8, 16, "bf16", seed=23),
+    # wide router with E % 8 != 0
+    "wide_e20": W("wide_e20", 150, 200, 20, 3, 96, 4, 8, "bf16", seed=22),
 }
 
 _cache = {}
@@ -73,7 +78,8 @@ def test_route(name):
     check_routing(w, host(logits), host(idx), host(wt), ref["logits"])
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
+                                  "wide_ksplit", "wide_e20"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
