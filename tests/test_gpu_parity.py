@@ -55,6 +55,9 @@ SMALL = {
     "wide_ksplit": W("wide_ksplit", 300, 1032, 40, 4, 64, 8, 16, "bf16", seed=23),
     # wide router with E % 8 != 0
     "wide_e20": W("wide_e20", 150, 200, 20, 3, 96, 4, 8, "bf16", seed=22),
+    # top-k with 2 (96 experts) and 8 (384 experts) values per lane
+    "topk_e96": W("topk_e96", 130, 64, 96, 6, 32, 0, 16, "bf16", seed=24),
+    "topk_e384": W("topk_e384", 70, 128, 384, 8, 32, 16, 32, "bf16", seed=25),
 }
 
 _cache = {}
@@ -79,7 +82,8 @@ def test_route(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
-                                  "wide_ksplit", "wide_e20"])
+                                  "wide_ksplit", "wide_e20", "topk_e96",
+                                  "topk_e384"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
