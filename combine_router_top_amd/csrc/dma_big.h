@@ -51,17 +51,35 @@ constexpr int BD_SLOT = BD_AOFF + BD_BM * DT_KS * 2;  // bytes per ring slot (32
 #define MOE_BD_NS 4
 #endif
 constexpr int BD_NS = MOE_BD_NS;                   // ring slots
-constexpr int BD_CNT = 4;                          // copy instructions per wave per stage
 static_assert(BD_NS == 4 || BD_NS == 5, "ring of 4 or 5 slots");
 // steps per unrolled trip: fragments alternate between two register sets, so
 // a trip returns to the first set after an even number of steps
 constexpr int BD_TL = BD_NS % 2 ? 2 * BD_NS : BD_NS;
 
+// NW waves (8: two per SIMD, or 4: one per SIMD) in a (NW / 2) x 2 grid over
+// the 256 x 256 tile: wave w = (wm, wn) = (w % WPH, w / WPH) multiplies rows
+// 16 MT wm .. 16 MT wm + 16 MT - 1 by 128 weight columns (half wn).  Each
+// wave copies RPW rows of its weight half-panel hp = w / WPH (CW copies of 4
+// rows) and CA of the 16 A copies (16 rows each) per stage.
+template <int NW>
+struct BdCfg {
+  static_assert(NW == 8 || NW == 4, "8 or 4 waves");
+  static constexpr int WPH = NW / 2;        // waves per column half and per weight half-panel
+  static constexpr int MT = 16 / WPH;       // m-tiles per wave
+  static constexpr int RPW = 32 / WPH;      // weight rows a wave copies per stage
+  static constexpr int CW = RPW / 4;        // weight copies per wave per stage
+  static constexpr int CA = 16 / NW;        // A copies per wave per stage
+  static constexpr int CNT = CW + CA;       // copy instructions per wave per stage
+  static constexpr int NP = CW / 2;         // weight lane offsets: copies 2p, 2p + 1 share one
+};
+
 // Per-thread fixed state of the K loop.
+template <int NW>
 struct BdCtx {
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[2];   // A copies a = wave, wave + 8: lane source offsets (bytes) at k 0
-  uint32_t vb;      // weight copy 0: lane source offset at stage row 0; copy 1 reads 4 rows on
+  uint32_t va[BdCfg<NW>::CA];   // A copies a = wave + NW v: lane source offsets (bytes) at k 0
+  uint32_t vb[BdCfg<NW>::NP];   // weight copy 2p: lane source offset at stage row 0; copy
+                                // 2p + 1 reads 4 rows further
   uint32_t ldb2;    // bytes per row of B
   int bdst;         // first weight destination of this wave inside a slot
   int adst;         // first A destination of this wave inside a slot
@@ -85,8 +103,9 @@ __device__ __forceinline__ void bd_copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds
 }
 
 // Stage st into ring slot J.
-template <int J>
-__device__ __forceinline__ void bd_issue(const BdCtx& c, int st) {
+template <int J, int NW>
+__device__ __forceinline__ void bd_issue(const BdCtx<NW>& c, int st) {
+  using Cfg = BdCfg<NW>;
   // recomputed per stage from one base, so that the unrolled loop does not
   // keep an address per slot and copy in scalar registers
   uint32_t b = c.lbase;
@@ -94,33 +113,35 @@ __device__ __forceinline__ void bd_issue(const BdCtx& c, int st) {
   const uint32_t slot = b + (uint32_t)(J * BD_SLOT);
   const uint32_t k0 = (uint32_t)(st * DT_KS);
   const uint32_t sb = k0 * c.ldb2;
-  bd_copy16(c.rb, slot + c.bdst, c.vb, sb);
-  bd_copy16(c.rb, slot + c.bdst + 1024, c.vb, sb + 4 * c.ldb2);
-  bd_copy16(c.ra, slot + c.adst, c.va[0], k0 * 2);
-  bd_copy16(c.ra, slot + c.adst + 8 * 1024, c.va[1], k0 * 2);
+#pragma unroll
+  for (int u = 0; u < Cfg::CW; ++u)
+    bd_copy16(c.rb, slot + c.bdst + 1024 * u, c.vb[u >> 1], sb + (u & 1) * 4 * c.ldb2);
+#pragma unroll
+  for (int v = 0; v < Cfg::CA; ++v) bd_copy16(c.ra, slot + c.adst + NW * 1024 * v, c.va[v], k0 * 2);
 }
 
-// The fragments of one stage: 4 A fragments (m-tiles) and 8 weight fragments
-// (n-tiles).
+// The fragments of one stage: MT A fragments (m-tiles) and 8 weight
+// fragments (n-tiles).
+template <int MT>
 struct BdFrag {
-  bf16x8 x[4], w[8];
+  bf16x8 x[MT], w[8];
 };
 
 // Reads of the stage in slot J: the A fragments, and the weight fragment of
 // n-tile t.  kleft < DT_KS (last stage only, MASK) zeroes both fragments for
 // k past the end, whatever the slot holds there.
-template <int J, bool MASK>
-__device__ __forceinline__ void bd_read_x(const BdCtx& c, const char* ring, int kleft, BdFrag& f) {
+template <int J, bool MASK, int NW, int MT>
+__device__ __forceinline__ void bd_read_x(const BdCtx<NW>& c, const char* ring, int kleft, BdFrag<MT>& f) {
   const char* slot = ring + J * BD_SLOT;
   const bool zero = MASK && 8 * ((threadIdx.x & 63) >> 4) >= kleft;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     f.x[mt] = *reinterpret_cast<const bf16x8*>(slot + BD_AOFF + c.aoff + 1024 * mt);
     if (zero) f.x[mt] = bf16x8{};
   }
 }
-template <int J, bool MASK, bool SWIGLU>
-__device__ __forceinline__ void bd_read_w(const char* ring, int wx, int t, int kleft, BdFrag& f) {
+template <int J, bool MASK, bool SWIGLU, int MT>
+__device__ __forceinline__ void bd_read_w(const char* ring, int wx, int t, int kleft, BdFrag<MT>& f) {
   const char* slot = ring + J * BD_SLOT;
   const bool zero = MASK && 8 * ((threadIdx.x & 63) >> 4) >= kleft;
   const int off = SWIGLU ? (wx ^ (32 * (t & 3))) + (t >> 2) * BD_HP : wx ^ (32 * t);
@@ -138,12 +159,14 @@ __device__ __forceinline__ void bd_sync() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// bd_sync with n (0..4) newer stages left in flight (n wave-uniform).
+// bd_sync with n (0..4) newer stages of CNT copies left in flight (n
+// wave-uniform).
+template <int CNT>
 __device__ __forceinline__ void bd_sync_n(int n) {
-  if (n >= 4) bd_sync<4 * BD_CNT>();
-  else if (n == 3) bd_sync<3 * BD_CNT>();
-  else if (n == 2) bd_sync<2 * BD_CNT>();
-  else if (n == 1) bd_sync<BD_CNT>();
+  if (n >= 4) bd_sync<4 * CNT>();
+  else if (n == 3) bd_sync<3 * CNT>();
+  else if (n == 2) bd_sync<2 * CNT>();
+  else if (n == 1) bd_sync<CNT>();
   else bd_sync<0>();
 }
 
@@ -151,19 +174,22 @@ __device__ __forceinline__ void bd_sync_n(int n) {
 // stage st + 1 and barrier (every wave then holds stage st in registers, so
 // slot J is free), refill slot J with stage st + BD_NS, then read stage st + 1
 // into G while multiplying F.  GUARD: the form with range conditions (tail).
-template <int J, bool GUARD, bool SWIGLU>
-__device__ __forceinline__ void bd_step(const BdCtx& c, char* ring, int st, int nst, int K,
-                                        BdFrag& F, BdFrag& G, f32x4 (&acc)[4][8]) {
+template <int J, bool GUARD, bool SWIGLU, int NW>
+__device__ __forceinline__ void bd_step(const BdCtx<NW>& c, char* ring, int st, int nst, int K,
+                                        BdFrag<BdCfg<NW>::MT>& F, BdFrag<BdCfg<NW>::MT>& G,
+                                        f32x4 (&acc)[BdCfg<NW>::MT][8]) {
+  using Cfg = BdCfg<NW>;
+  constexpr int MT = Cfg::MT;
   if (GUARD && st >= nst) return;
   const bool next = !GUARD || st + 1 < nst;
   if (next) {
     // issued stages after st + 1: BD_NS - 2, fewer near the end
-    if (!GUARD) bd_sync<(BD_NS - 2) * BD_CNT>();
-    else bd_sync_n(min(nst - 2 - st, BD_NS - 2));
+    if (!GUARD) bd_sync<(BD_NS - 2) * Cfg::CNT>();
+    else bd_sync_n<Cfg::CNT>(min(nst - 2 - st, BD_NS - 2));
     if (!GUARD || st + BD_NS < nst) bd_issue<J % BD_NS>(c, st + BD_NS);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // stage st + 1's A fragments, then per n-tile t: the 4 products of F's
+  // stage st + 1's A fragments, then per n-tile t: the MT products of F's
   // fragment t and the reads of G's fragment t, which can take its registers
   const int kl = K - (st + 1) * DT_KS;
   int wx = c.wx;
@@ -172,33 +198,34 @@ __device__ __forceinline__ void bd_step(const BdCtx& c, char* ring, int st, int 
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt][t] = mfma16(F.w[t], F.x[mt], acc[mt][t]);
+    for (int mt = 0; mt < MT; ++mt) acc[mt][t] = mfma16(F.w[t], F.x[mt], acc[mt][t]);
     if (next) bd_read_w<(J + 1) % BD_NS, GUARD, SWIGLU>(ring, wx, t, kl, G);
   }
   if (next) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int J, bool GUARD, bool SWIGLU>
-__device__ __forceinline__ void bd_trip(const BdCtx& c, char* ring, int st, int nst, int K,
-                                        BdFrag& F, BdFrag& G, f32x4 (&acc)[4][8]) {
+template <int J, bool GUARD, bool SWIGLU, int NW>
+__device__ __forceinline__ void bd_trip(const BdCtx<NW>& c, char* ring, int st, int nst, int K,
+                                        BdFrag<BdCfg<NW>::MT>& F, BdFrag<BdCfg<NW>::MT>& G,
+                                        f32x4 (&acc)[BdCfg<NW>::MT][8]) {
   // fragments alternate between F and G from step to step
   bd_step<J, GUARD, SWIGLU>(c, ring, st + J, nst, K, F, G, acc);
   if constexpr (J + 1 < BD_TL) bd_trip<J + 1, GUARD, SWIGLU>(c, ring, st, nst, K, G, F, acc);
 }
 
-template <int J>
-__device__ __forceinline__ void bd_prologue(const BdCtx& c, char* ring, int nst) {
+template <int J, int NW>
+__device__ __forceinline__ void bd_prologue(const BdCtx<NW>& c, int nst) {
   if constexpr (J < BD_NS) {
     if (J < nst) bd_issue<J>(c, J);
-    bd_prologue<J + 1>(c, ring, nst);
+    bd_prologue<J + 1>(c, nst);
   }
 }
 
@@ -208,59 +235,63 @@ __device__ __forceinline__ void bd_prologue(const BdCtx& c, char* ring, int nst)
 // N columns (row 0 = k 0) and brows readable rows; klen <= brows.  Columns:
 // weight column block nt (GEMM-1: 128 columns of B1 and the same of B3).
 // Rows past R, k past klen and columns past N read zeros or meet zeros.
-// lda, N multiples of 8.  ring: BD_NS * BD_SLOT bytes of LDS.  All 512
-// threads call; the caller separates two tiles of one workgroup with a barrier.
-// acc[mt][t] of lane (i, g) of wave (wm, wn) = (w & 3, w >> 2): row
-// 64 wm + 16 mt + i, weight columns 16 t + 4 g .. + 3 of the wave's range
+// lda, N multiples of 8.  ring: BD_NS * BD_SLOT bytes of LDS.  All 64 NW
+// threads call; the caller separates two tiles of one workgroup with a
+// barrier.  acc[mt][t] of lane (i, g) of wave (wm, wn): row
+// 16 MT wm + 16 mt + i, weight columns 16 t + 4 g .. + 3 of the wave's range
 // (GEMM-1: h columns 128 nt + 64 wn + 16 (t & 3) + 4 g, of W1 for t < 4 and of
 // W3 for t >= 4; otherwise columns 256 nt + 128 wn + 16 t + 4 g).
-template <bool SWIGLU>
+template <bool SWIGLU, int NW>
 __device__ __forceinline__ void bd_accum(const bf16_t* __restrict__ A, int64_t lda,
                                          const bf16_t* __restrict__ B1, const bf16_t* __restrict__ B3,
                                          int64_t brows, int klen, int N, int r0, int R, int nt,
                                          const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
-                                         char* ring, f32x4 (&acc)[4][8]) {
+                                         char* ring, f32x4 (&acc)[BdCfg<NW>::MT][8]) {
+  using Cfg = BdCfg<NW>;
+  constexpr int MT = Cfg::MT;
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nst = (klen + DT_KS - 1) / DT_KS;
   if (nst <= 0) return;
-  BdCtx c;
-  // weight copies: half-panel hp = wave >> 2, rows 8 (wave & 3) .. + 7, four
-  // rows (16 lanes each) per instruction; rows j and j + 4 share sigma
-  const int hp = wave >> 2;
+  BdCtx<NW> c;
+  // weight copies: half-panel hp = wave / WPH, rows RPW (wave % WPH) .. + RPW
+  // - 1, four rows (16 lanes each) per copy; rows j and j + 4 of a copy pair
+  // share sigma
+  const int hp = wave / Cfg::WPH, wq = wave % Cfg::WPH;
   const bf16_t* Bp = SWIGLU && hp ? B3 : B1;
   const int colbase = SWIGLU ? 128 * nt : 256 * nt + 128 * hp;
   c.rb = gc_rsrc(Bp, (uint32_t)(brows * N * 2));
   c.ldb2 = (uint32_t)(N * 2);
-  {
-    const int j = 8 * (wave & 3) + (lane >> 4);
+#pragma unroll
+  for (int q = 0; q < Cfg::NP; ++q) {
+    const int j = Cfg::RPW * wq + 8 * q + (lane >> 4);
     const int sig = (j & 3) | (((j >> 3) & 1) << 2);
     const int col = colbase + 8 * ((lane & 15) ^ (2 * sig));
-    c.vb = col < N ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
+    c.vb[q] = col < N ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
   }
-  c.bdst = hp * BD_HP + 2048 * (wave & 3);
+  c.bdst = hp * BD_HP + Cfg::RPW * wq * BD_HPROW;
   c.lbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dt_lds_t*)ring);
-  // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row.
+  // A copies: copy a covers tile rows 16 a .. 16 a + 15, 4 lanes a row.
   // Without a row map the descriptor ends at the block's last element, k = klen
   // of row R - 1 (A may start inside a row: a K range of a wider matrix)
   c.ra = rows ? gc_rsrc(A, abytes)
               : gc_rsrc(A + (int64_t)r0 * lda, (uint32_t)(((int64_t)(R - 1) * lda + klen) * 2));
 #pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int r = 16 * (wave + 8 * v) + (lane >> 2);
+  for (int v = 0; v < Cfg::CA; ++v) {
+    const int r = 16 * (wave + NW * v) + (lane >> 2);
     const int rr = min(r, R - 1);
     const uint32_t row = rows ? (uint32_t)(rows[r0 + rr] / rdiv) : (uint32_t)rr;
     c.va[v] = (row * (uint32_t)lda + 8u * (uint32_t)((lane & 3) ^ dt_swa(r))) * 2u;
   }
   c.adst = BD_AOFF + 1024 * wave;
   // fragment reads
-  const int wm = wave & 3, wn = wave >> 2;
-  c.aoff = (64 * wm + i) * 64 + 16 * (g ^ dt_swa(i));
+  const int wm = wq, wn = hp;
+  c.aoff = (16 * MT * wm + i) * 64 + 16 * (g ^ dt_swa(i));
   // weight fragment of n-tile ti of a half-panel: rows 8 g + i / 4 (and + 4),
   // columns 16 ti + 4 (i % 4) .. + 3 -> byte row * 256 + (32 (ti ^ sigma) +
   // 8 (i % 4)), sigma = (i / 4) | (g & 1) << 2; the XOR touches bits 5..7 only
@@ -268,9 +299,9 @@ __device__ __forceinline__ void bd_accum(const bf16_t* __restrict__ A, int64_t l
   const int wlane = (8 * g + (i >> 2)) * BD_HPROW + 32 * sig + 8 * (i & 3);
   c.wx = SWIGLU ? (wlane ^ (32 * 4 * wn)) : wlane + wn * BD_HP;
 
-  bd_prologue<0>(c, ring, nst);   // stages 0 .. BD_NS - 1 into every slot
-  bd_sync_n(min(nst - 1, BD_NS - 1));
-  BdFrag F, G;
+  bd_prologue<0>(c, nst);   // stages 0 .. BD_NS - 1 into every slot
+  bd_sync_n<Cfg::CNT>(min(nst - 1, BD_NS - 1));
+  BdFrag<MT> F, G;
   bd_read_x<0, true>(c, ring, klen, F);
 #pragma unroll
   for (int t = 0; t < 8; ++t) bd_read_w<0, true, SWIGLU>(ring, c.wx, t, klen, F);
@@ -281,28 +312,30 @@ __device__ __forceinline__ void bd_accum(const bf16_t* __restrict__ A, int64_t l
   bd_trip<0, true, SWIGLU>(c, ring, st + BD_TL, nst, klen, F, G, acc);
 }
 
-// One 256 x 256 tile: rows [r0, r0 + R) (1 <= R <= 256) of A, where A row r is
-// A[r0 + r] or, with a row map, row rows[r0 + r] / rdiv of the abytes-byte
-// matrix A; weight column block nt of expert e.  K and N multiples of 8.
+// One 256 x 256 tile on NW waves: rows [r0, r0 + R) (1 <= R <= 256) of A,
+// where A row r is A[r0 + r] or, with a row map, row rows[r0 + r] / rdiv of
+// the abytes-byte matrix A; weight column block nt of expert e.  K and N
+// multiples of 8.
 //   SWIGLU: C[r0 + r][128 nt + h] = rnd(SiLU(A W1) * (A W3)), B1/B3 = [E][K][N]
 //   else:   C[r0 + r][256 nt + n] = rnd(A W2),                 B1 = [E][K][N]
-template <bool SWIGLU>
+template <bool SWIGLU, int NW>
 __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                         const bf16_t* __restrict__ B3, int K, int N,
                                         bf16_t* __restrict__ C, int e, int r0, int R, int nt,
                                         const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
                                         char* ring) {
+  constexpr int MT = BdCfg<NW>::MT;
   const int64_t estride = (int64_t)K * N;
-  f32x4 acc[4][8];
-  bd_accum<SWIGLU>(A, K, B1 + e * estride, SWIGLU ? B3 + e * estride : nullptr, K, K, N, r0, R, nt,
-                   rows, rdiv, abytes, ring, acc);
+  f32x4 acc[MT][8];
+  bd_accum<SWIGLU, NW>(A, K, B1 + e * estride, SWIGLU ? B3 + e * estride : nullptr, K, K, N, r0, R,
+                       nt, rows, rdiv, abytes, ring, acc);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 3, wn = wave >> 2;
+  const int wm = wave % BdCfg<NW>::WPH, wn = wave / BdCfg<NW>::WPH;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = 64 * wm + 16 * mt + i;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = 16 * MT * wm + 16 * mt + i;
 #pragma unroll
     for (int t = 0; t < (SWIGLU ? 4 : 8); ++t) {
       const int col = SWIGLU ? 128 * nt + 64 * wn + 16 * t + 4 * g : 256 * nt + 128 * wn + 16 * t + 4 * g;

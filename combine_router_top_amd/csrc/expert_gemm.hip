@@ -288,7 +288,10 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
 // weight columns, two waves per SIMD).
 constexpr int XB_BM = BD_BM;
 constexpr int XB_BN = BD_BN;    // weight columns per tile (GEMM-1: 128 of W1 + 128 of W3)
-constexpr int XB_NW = 8;        // waves per workgroup
+#ifndef MOE_XB_NW
+#define MOE_XB_NW 8
+#endif
+constexpr int XB_NW = MOE_XB_NW;  // waves per workgroup (8: two per SIMD; 4: one per SIMD)
 #ifndef MOE_XB_TH
 #define MOE_XB_TH 320
 #endif
@@ -352,7 +355,7 @@ __device__ BigTile big_tile_at(int L, const int32_t* __restrict__ offsets, int e
   return bt;
 }
 
-static_assert(XGThin::NW == 8 && XB_NW == 8, "one workgroup size for all streamed tile classes");
+static_assert(XGThin::NW == 8, "one workgroup size for all streamed tile classes");
 // The thin tiles borrow the medium ring slots: the A stages in slot 0, the
 // W3 -> W1 accumulator exchange in slots 1 and 2 (half of the pairs each).
 static_assert(2 * gc_lds_elems<XGThin::NW, XGThin::CPL, XGThin::MTMAX>() <= DT_SLOT,
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     bt.R = __builtin_amdgcn_readfirstlane(bt.R);
     bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
     __syncthreads();   // every wave has read the table before the copies overwrite it
-    bd_tile<SWIGLU>(A, B1, B3, K, N, C, bt.e, bt.r0, bt.R, bt.nt, rm.rows, rm.div, rm.bytes, ring);
+    bd_tile<SWIGLU, XB_NW>(A, B1, B3, K, N, C, bt.e, bt.r0, bt.R, bt.nt, rm.rows, rm.div, rm.bytes, ring);
   }
 }
 
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void gemm_signal_kernel(
   bt.r0 = tm * XB_BM;
   bt.R = min(XB_BM, M - bt.r0);
   bt.nt = tn;
-  bd_tile<false>(A, B, nullptr, K, N, C, 0, bt.r0, bt.R, bt.nt, nullptr, 1, 0, ring);
+  bd_tile<false, XB_NW>(A, B, nullptr, K, N, C, 0, bt.r0, bt.R, bt.nt, nullptr, 1, 0, ring);
   // every thread's stores of the tile complete and visible at the scope,
   // then one release store of the flag
   if (system_scope) __threadfence_system();
