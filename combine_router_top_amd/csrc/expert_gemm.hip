@@ -100,18 +100,19 @@ constexpr int XG_WUNIT = 64;
 constexpr int XG_WT_THIN = XGThin::COLS / XG_WUNIT;
 static_assert(XG_WT_THIN * XG_WUNIT == XGThin::COLS, "thin columns a multiple of the work unit");
 
-// Blocks of class `cls` of one expert with `cnt` rows (0 for the other class).
-__device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls, int mcols) {
+// Blocks of class `cls` of one expert with `cnt` rows (0 for the other class);
+// thin blocks span tcols weight columns, medium ones mcols.
+__device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls, int mcols, int tcols) {
   if (cnt <= 0 || cnt >= th || (cnt <= XG_THIN_MAX ? 0 : 1) != cls) return 0;
-  if (cls == 0) return (ncols + XGThin::COLS - 1) / XGThin::COLS;
+  if (cls == 0) return (ncols + tcols - 1) / tcols;
   return (cnt + XM_BM - 1) / XM_BM * ((ncols + mcols - 1) / mcols);
 }
 
 // Schedule from `offsets` (computed by every workgroup, a few hundred cycles).
 // Experts in [e_begin, e_end) with fewer than `th` rows contribute (row block,
 // column block) pairs of their tile class.  The blocks are listed thin class
-// first, then medium, each by ascending expert; a thin block weighs XG_WT_THIN,
-// a medium one mcols / XG_WUNIT, and block i starts at the running sum of the
+// first, then medium, each by ascending expert; a thin block weighs tcols /
+// XG_WUNIT, a medium one mcols / XG_WUNIT, and block i starts at the running sum of the
 // weights before it.  XCD x (workgroup id mod 8 on this part) takes the blocks that start in
 // [ceil(x W / 8), ceil((x + 1) W / 8)) of the total work W, the q-th of them
 // going to its q-th workgroup.  Every XCD thus gets an equal share of the
@@ -121,7 +122,7 @@ __device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls, in
 // 8 ceil(ceil(W / 8) / min weight) workgroups at most.  R = 0 means "exit".
 // `pre` holds 2 (XG_MAXN + 1) ints.
 __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, int e_end,
-                             int th, int ncols, int mcols, int* pre) {
+                             int th, int ncols, int mcols, int tcols, int* pre) {
   const int ne = e_end - e_begin;
   int* prew = pre + XG_MAXN + 1;
   if (threadIdx.x < 64) {
@@ -130,8 +131,8 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
     for (int j0 = 0; j0 < ne; j0 += 64) {
       const int j = j0 + lane;
       const int cnt = j < ne ? offsets[e_begin + j + 1] - offsets[e_begin + j] : 0;
-      int xt = xg_blocks(cnt, th, ncols, 0, mcols);
-      int xw = xg_blocks(cnt, th, ncols, 1, mcols);
+      int xt = xg_blocks(cnt, th, ncols, 0, mcols, tcols);
+      int xw = xg_blocks(cnt, th, ncols, 1, mcols, tcols);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int yt = __shfl_up(xt, off);
@@ -148,15 +149,16 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   RowBlock rb{0, 0, 0, 0, 0};
   const int nth = pre[XG_MAXN], nwd = prew[XG_MAXN];
   const int wm = mcols / XG_WUNIT;                   // work of a medium block
-  const int wth = XG_WT_THIN * nth;                  // work of the thin blocks
+  const int wt = tcols / XG_WUNIT;                   // work of a thin block
+  const int wth = wt * nth;                          // work of the thin blocks
   const int W = wth + wm * nwd;
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int w0 = (xcd * W + 7) >> 3, w1 = ((xcd + 1) * W + 7) >> 3;
   // first block starting at or after w0, then this workgroup's block
-  const int i0 = w0 <= wth ? (w0 + XG_WT_THIN - 1) / XG_WT_THIN : nth + (w0 - wth + wm - 1) / wm;
+  const int i0 = w0 <= wth ? (w0 + wt - 1) / wt : nth + (w0 - wth + wm - 1) / wm;
   const int i = i0 + q;
   if (i >= nth + nwd) return rb;
-  const int start = i < nth ? XG_WT_THIN * i : wth + wm * (i - nth);
+  const int start = i < nth ? wt * i : wth + wm * (i - nth);
   if (start >= w1) return rb;
   rb.cls = i < nth ? 0 : 1;
   const int* P = rb.cls ? prew : pre;
@@ -171,7 +173,7 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   const int o = offsets[e];
   const int cnt = offsets[e + 1] - o;
   const int bm = rb.cls ? XM_BM : XGThin::BM;
-  const int cols = rb.cls ? mcols : XGThin::COLS;
+  const int cols = rb.cls ? mcols : tcols;
   const int nblk = (ncols + cols - 1) / cols;
   const int jb = local / nblk;
   rb.nb = local - jb * nblk;
@@ -253,8 +255,8 @@ template <class Cfg, bool SWIGLU>
 __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                              const bf16_t* __restrict__ B3, int K, int N,
                                              bf16_t* __restrict__ C, const RowBlock& rb,
-                                             const RowMap& rm, int wave, bf16_t* As, float* xch0,
-                                             float* xch1) {
+                                             const RowMap& rm, int wave, int tcols, bf16_t* As,
+                                             float* xch0, float* xch1) {
   const int i = threadIdx.x & 15;
   int col;
   const bf16_t* Bl;
@@ -262,8 +264,9 @@ __device__ __forceinline__ void stream_block(const bf16_t* __restrict__ A, const
   if (SWIGLU) {  // lower half of the waves streams W1, upper half the same columns of W3
     col = rb.nb * Cfg::WG_H + (wave % (Cfg::NW / 2)) * Cfg::HW + Cfg::CPL * i;
     Bl = ((wave < Cfg::NW / 2) ? B1 : B3) + rb.e * estride;
-  } else {       // output columns per wave
-    col = rb.nb * Cfg::WG_O + wave * Cfg::OW + Cfg::CPL * i;
+  } else {       // output columns per wave; a block of tcols < WG_O columns
+                 // leaves its last waves idle (columns past N: zero loads, no stores)
+    col = wave * Cfg::OW < tcols ? rb.nb * tcols + wave * Cfg::OW + Cfg::CPL * i : N;
     Bl = B1 + rb.e * estride;
   }
   const int mt = (rb.R + 15) >> 4;
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
                                                                      const bf16_t* __restrict__ B3,
                                                                      int K, int N,
                                                                      bf16_t* __restrict__ C, int th,
-                                                                     int mcols, RowMap rm) {
+                                                                     int mcols, int tcols, RowMap rm) {
   __shared__ __attribute__((aligned(16))) char S0[DT_SLOT];
   __shared__ __attribute__((aligned(16))) char S1[DT_SLOT];
   __shared__ __attribute__((aligned(16))) char S2[DT_SLOT];
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   __shared__ int pre[2 * (XG_MAXN + 1)];
   // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
   const int ncols = SWIGLU ? 2 * N : N;
-  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, mcols, pre);
+  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, mcols, SWIGLU ? XGThin::COLS : tcols, pre);
   // values from LDS and the wave index are wave-uniform; say so, so that
   // pointers and buffer descriptors built from them live in scalar registers
   rb.e = __builtin_amdgcn_readfirstlane(rb.e);
@@ -393,8 +396,9 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   if (rb.R <= 0) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (rb.cls == 0) {
-    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, rm, wave, reinterpret_cast<bf16_t*>(S0),
-                                 reinterpret_cast<float*>(S1), reinterpret_cast<float*>(S2));
+    stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, rm, wave, SWIGLU ? XGThin::COLS : tcols,
+                                 reinterpret_cast<bf16_t*>(S0), reinterpret_cast<float*>(S1),
+                                 reinterpret_cast<float*>(S2));
     return;
   }
   const DtSlots slots{{S0, S1, S2}, dtab};
@@ -608,25 +612,43 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
       }
       return best;
     };
+    // Thin column blocks of the down projection: when the expected segment is
+    // thin, the width (512, 448 or 384 output columns; the last waves of a
+    // narrower block idle) whose block count fills the last round best, e.g.
+    // 7168 columns x 32 experts: 448 gives exactly 2 rounds where 512 gives
+    // 1.75.  GEMM-1 keeps 512 (its W1 and W3 halves pair 256 h columns).
+    auto pick_tcols = [&](int ncols) {
+      if (mean_rows > XG_THIN_MAX) return XGThin::COLS;
+      int best = XGThin::COLS;
+      double best_fill = 0.0;
+      for (int cw = XGThin::COLS; cw >= 384; cw -= XGThin::OW) {
+        const int64_t nb = (int64_t)ne * ((ncols + cw - 1) / cw);
+        const double fill = (double)nb / (double)(((nb + cus - 1) / cus) * cus);
+        if (fill > best_fill + 1e-9) { best_fill = fill; best = cw; }
+      }
+      return best;
+    };
     // Streaming grid: the total work W of schedule() (units of XG_WUNIT
-    // columns).  A thin expert is one row block of nt blocks of weight
-    // XG_WT_THIN, a medium one ceil(cnt / BM) row blocks of nw blocks of
+    // columns).  A thin expert is one row block of nt blocks of weight wt =
+    // tcols / XG_WUNIT, a medium one ceil(cnt / BM) row blocks of nw blocks of
     // weight wm; a streamed expert has fewer than min(T + 1, th) rows, and the
     // local row counts add up to at most rows_max.  Each XCD's blocks start in
-    // a window of ceil(W / 8) at least min(XG_WT_THIN, wm) apart.
+    // a window of ceil(W / 8) at least min(wt, wm) apart.
     const int64_t rbmax = (std::min<int64_t>(p.T, (int64_t)th - 1) + XM_BM - 1) / XM_BM;
-    auto grid = [&](int ncols, int mcols) {
+    auto grid = [&](int ncols, int mcols, int tcols) {
       const int64_t wm = mcols / XG_WUNIT;
-      const int64_t nt = (ncols + XGThin::COLS - 1) / XGThin::COLS;
+      const int64_t wt = tcols / XG_WUNIT;
+      const int64_t nt = (ncols + tcols - 1) / tcols;
       const int64_t nw = (ncols + mcols - 1) / mcols;
-      const int64_t per_e = std::max<int64_t>(XG_WT_THIN * nt, wm * nw);
+      const int64_t per_e = std::max<int64_t>(wt * nt, wm * nw);
       const int64_t w_rows = ne * per_e + wm * ((p.rows_max * nw + XM_BM - 1) / XM_BM);
-      const int64_t w_exp = ne * std::max<int64_t>(XG_WT_THIN * nt, wm * rbmax * nw);
+      const int64_t w_exp = ne * std::max<int64_t>(wt * nt, wm * rbmax * nw);
       const int64_t w = std::min(w_rows, w_exp);
-      const int64_t wmin = std::min<int64_t>(XG_WT_THIN, wm);
+      const int64_t wmin = std::min<int64_t>(wt, wm);
       return (unsigned)(8 * ((((w + 7) / 8) + wmin - 1) / wmin));
     };
     const int mc1 = pick_mcols(2 * p.f), mc2 = pick_mcols(p.d);
+    const int tc1 = XGThin::COLS, tc2 = pick_tcols(p.d);
     // Large-tile grid (dense-like routing only): its tiles, the sum over
     // experts with n_e >= XB_TH of ceil(n_e / BM) <= rows_max / BM +
     // min(ne, rows_max / XB_TH) m-tiles, times ntn, each with its own
@@ -641,9 +663,9 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn, rm1);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f, mc1)), dim3(64 * XGThin::NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f, mc1, tc1)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, mc1, rm1);
+                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, mc1, tc1, rm1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (big) {
       const int ntn = (p.d + 255) / 256;
@@ -652,9 +674,9 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, ntn, rm2);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d, mc2)), dim3(64 * XGThin::NW), 0, st,
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d, mc2, tc2)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, mc2, rm2);
+                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, mc2, tc2, rm2);
     return hipGetLastError();
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);

@@ -58,6 +58,10 @@ SMALL = {
     # top-k with 2 (96 experts) and 8 (384 experts) values per lane
     "topk_e96": W("topk_e96", 130, 64, 96, 6, 32, 0, 16, "bf16", seed=24),
     "topk_e384": W("topk_e384", 70, 128, 384, 8, 32, 16, 32, "bf16", seed=25),
+    # thin down-projection blocks of 448 and 384 output columns (the width
+    # that fills the last round: 32 x 16 and 16 x 16 blocks)
+    "thin_tcols448": W("thin_tcols448", 64, 7168, 32, 2, 64, 0, 32, "bf16", seed=26),
+    "thin_tcols384": W("thin_tcols384", 48, 6144, 16, 2, 64, 0, 16, "bf16", seed=27),
 }
 
 _cache = {}
