@@ -62,9 +62,9 @@ SMALL = {
     # that fills the last round: 32 x 16 and 16 x 16 blocks)
     "thin_tcols448": W("thin_tcols448", 64, 7168, 32, 2, 64, 0, 32, "bf16", seed=26),
     "thin_tcols384": W("thin_tcols384", 48, 6144, 16, 2, 64, 0, 16, "bf16", seed=27),
-    # medium GEMM-1 blocks of 512 weight columns over h columns in two
-    # 128-column pieces (64 experts x 1024 h columns, ~50 rows each)
-    "medium_pieces": W("medium_pieces", 1600, 64, 64, 2, 1024, 0, 64, "bf16", seed=28),
+    # medium GEMM-1 blocks of the full 512 weight columns at a small size
+    # (64 experts x 1024 h columns, ~50 rows each: 256 blocks fill one round)
+    "medium_w512": W("medium_w512", 1600, 64, 64, 2, 1024, 0, 64, "bf16", seed=28),
 }
 
 _cache = {}
