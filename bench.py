@@ -449,6 +449,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / a.steps
+    # step-time distribution: the same number of steps again, an event after each
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    sev[0].record(stream)
+    for i in range(a.steps):
+        step()
+        sev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(a.steps)])
+    step_stats = {"p10_ms": float(np.percentile(per_step, 10)), "median_ms": float(np.median(per_step)),
+                  "p90_ms": float(np.percentile(per_step, 90)), "steps": a.steps}
 
     # each ABI call on its own, HIP events on the launch stream between calls
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
@@ -477,17 +487,41 @@ def main():
         if it >= 2:
             for j, n in enumerate(names):
                 tot[n] += ev[j].elapsed_time(ev[j + 1])
+    # the same calls cold: before each, a 1 GiB fill evicts the L2s and the
+    # 256 MB MALL, so every operand comes from HBM
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = {n: 0.0 for n in names}
+    calls = [
+        lambda: M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt)),
+        lambda: M.dispatch(p, idx, d["x"], workspace=ws_d, out=dsp),
+        lambda: M.expert_gemm(p, dsp["x_packed"], dsp["offsets"], d["w1"], d["w3"], d["w2"], out=(h, yp)),
+        lambda: M.combine(p, yp, dsp["inv"], wt, out=y),
+    ]
+    cold_iters = 5
+    for it in range(cold_iters + 1):
+        for j, n in enumerate(names):
+            flush.fill_((it + j) & 0xFF)
+            ev[0].record(stream)
+            calls[j]()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if it >= 1:
+                cold[n] += ev[0].elapsed_time(ev[1])
+    del flush
+
     s = 2 if w.dtype == "bf16" else 4
     model = work_model(w, A, active, s)
-    phases = {}
-    for n in names:
-        sec = tot[n] / iters / 1e3
+
+    def phase(n, sec):
         ph = {"ms": sec * 1e3, "bytes": model[n]["bytes"], "flops": model[n]["flops"]}
         ph.update(roofline(model[n]["bytes"], model[n]["flops"], sec, w.dtype))
         if model[n]["flops"]:
             ph["tflops"] = model[n]["flops"] / sec / 1e12
             ph["mfma_frac"] = model[n]["flops"] / sec / MFMA_PEAK[w.dtype]
-        phases[n] = ph
+        return ph
+
+    phases = {n: phase(n, tot[n] / iters / 1e3) for n in names}
+    phases_cold = {n: phase(n, cold[n] / cold_iters / 1e3) for n in names}
 
     g = phases["expert_gemm"]
     roof = {k: g[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
@@ -516,6 +550,8 @@ def main():
                    "overlap": a.overlap},
         "roofline": roof,
         "phases": phases,
+        "phases_cold": phases_cold,
+        "step_stats": step_stats,
         "wall_ms_per_step": wall / a.steps * 1e3,
         "hbm_copy": copy,
         "input_gen_s": gen_s,
