@@ -132,6 +132,37 @@ def write_traffic(a):
     print(json.dumps(out))
 
 
+def hip_clock_mhz():
+    """Peak clock the HIP runtime reports for device 0 (hipDeviceAttributeClockRate,
+    value 5 in ROCm 7's hip_runtime_api.h, in kHz), or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(5), ctypes.c_int(0)) != 0:
+            return None
+        return v.value / 1e3
+    except OSError:
+        return None
+
+
+def run_env():
+    """Device, software versions and the clock the device reports (its maximum;
+    under a sustained MFMA load the effective clock is lower)."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    env = {"device": pr.name, "arch": getattr(pr, "gcnArchName", None),
+           "compute_units": pr.multi_processor_count,
+           "max_clock_mhz": hip_clock_mhz(),
+           "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        env["rocm"] = None
+    return env
+
+
 def work_model(w, A, active, s):
     """Algorithmic bytes and flops per call (what the method must move or
     compute; not the dense work it skips)."""
@@ -554,6 +585,7 @@ def main():
         "step_stats": step_stats,
         "wall_ms_per_step": wall / a.steps * 1e3,
         "hbm_copy": copy,
+        "env": run_env(),
         "input_gen_s": gen_s,
     }
     if not a.no_cpu_baseline:
