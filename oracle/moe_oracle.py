@@ -230,12 +230,15 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def _expert_rows(X: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray, dtype: str):
-    """One expert on float64 rows X: returns (h, y) after the rounding points."""
+def _expert_rows(X: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray, dtype: str,
+                 rounded: bool = True):
+    """One expert on float64 rows X: returns (h, y) after the rounding points
+    (with ``rounded=False``, in plain float64 with no rounding point)."""
+    r = dtype if rounded else "f64"
     a1 = X @ W1
     a3 = X @ W3
-    h = rnd(silu(a1) * a3, dtype)
-    y = rnd(h @ W2, dtype)
+    h = rnd(silu(a1) * a3, r)
+    y = rnd(h @ W2, r)
     return h, y
 
 
@@ -333,14 +336,20 @@ def gemm(A: np.ndarray, B: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def token_outputs(p, inputs: Dict[str, np.ndarray], topk_idx: np.ndarray, topk_w: np.ndarray,
-                  tokens: Sequence[int]) -> np.ndarray:
+                  tokens: Sequence[int], rounded: bool = True) -> np.ndarray:
     """Layer output rows y[t] for selected tokens only, under the given routing.
 
     Each token's output depends only on its own row of x and its own routing
     (the expert GEMM is row-independent), so this equals the corresponding
     rows of ``moe_layer`` and lets a full-size run be checked on a sample.
+
+    ``rounded=False`` skips the three rounding points of steps 7-8 (h,
+    y_packed, y) and returns the exact float64 layer on the same bf16 inputs:
+    a diagnostic of how far the stored-precision result sits from the exact
+    one, never a parity bar (the parity bar is the rounded result above).
     """
     dt = p.dtype
+    rt = dt if rounded else "f64"
     tokens = list(tokens)
     X = widen(np.asarray(inputs["x"])[tokens], dt)
     idx = np.asarray(topk_idx)
@@ -355,7 +364,7 @@ def token_outputs(p, inputs: Dict[str, np.ndarray], topk_idx: np.ndarray, topk_w
             continue
         rows = np.array([r for r, _ in pairs])
         _, y = _expert_rows(X[rows], widen(inputs["w1"][e], dt), widen(inputs["w3"][e], dt),
-                            widen(inputs["w2"][e], dt), dt)
+                            widen(inputs["w2"][e], dt), dt, rounded)
         for q, rj in enumerate(pairs):
             yslot[rj] = y[q]
     out = np.zeros((len(tokens), p.d), dtype=np.float64)
@@ -364,5 +373,5 @@ def token_outputs(p, inputs: Dict[str, np.ndarray], topk_idx: np.ndarray, topk_w
         for j in range(p.k):                     # slot order
             if (r, j) in yslot:
                 acc += W[t, j] * yslot[(r, j)]
-        out[r] = rnd(acc, dt)
+        out[r] = rnd(acc, rt)
     return out

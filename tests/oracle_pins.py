@@ -437,6 +437,36 @@ def pin_layer_rows_vs_tokens(O):
         assert np.allclose(r, o["y"][toks], rtol=2.0 ** -7 if dtype == "bf16" else 1e-12, atol=1e-300)
 
 
+def pin_token_outputs_unrounded(O):
+    """``token_outputs(rounded=False)`` is the exact float64 layer on the
+    stored inputs: pure-Python SwiGLU with no rounding, weighted by the local
+    gate weights in slot order; it differs from the rounded rows by at most a
+    few bf16 ulps, and for fp32 workloads the two are identical."""
+    for dtype in ("f32", "bf16"):
+        p, inp = _small_layer(O, dtype)
+        o = O.moe_layer(p, inp)
+        toks = [0, 9, 30, 47]
+        u = O.token_outputs(p, inp, o["topk_idx"], o["topk_w"], toks, rounded=False)
+        r = O.token_outputs(p, inp, o["topk_idx"], o["topk_w"], toks)
+        X = O.widen(inp["x"], dtype)
+        for q, t in enumerate(toks):
+            ref = np.zeros(p.d)
+            for j in range(p.k):
+                e = int(o["topk_idx"][t, j]) - p.expert_lo
+                if not 0 <= e < p.n_local:
+                    continue
+                _, y = _brute_swiglu([list(X[t])], O.widen(inp["w1"][e], dtype).tolist(),
+                                     O.widen(inp["w3"][e], dtype).tolist(),
+                                     O.widen(inp["w2"][e], dtype).tolist(), lambda v: v)
+                ref += float(o["topk_w"][t, j]) * y[0]
+            assert np.allclose(u[q], ref, rtol=1e-12, atol=1e-12)
+        if dtype == "f32":
+            assert np.array_equal(u, r)
+        else:
+            assert not np.array_equal(u, r)
+            assert np.allclose(u, r, rtol=2.0 ** -5, atol=2.0 ** -5 * np.abs(u).max())
+
+
 def pin_layer_padded(O):
     """The padded layer against the unpadded one: with C = the largest local
     count the outputs agree; with a smaller C they agree with the unpadded

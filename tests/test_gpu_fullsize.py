@@ -72,5 +72,11 @@ def test_layer_full_size(name):
     got = O.widen(yh[toks], w.dtype)
     rms = float(np.sqrt(np.mean(ref * ref)))
     err = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
-    print(f"[full-size] {name}: A={A} sampled {len(toks)} tokens, y err {err:.3e}", flush=True)
+    # diagnostic only: the same rows in exact float64, with no bf16 rounding
+    # point, show how much of the error is the stored precision itself
+    ex = O.token_outputs(w, inp, gi, gw, toks, rounded=False)
+    rms_x = float(np.sqrt(np.mean(ex * ex)))
+    err_x = float(np.max(np.abs(got - ex) / np.maximum(np.abs(ex), rms_x)))
+    print(f"[full-size] {name}: A={A} sampled {len(toks)} tokens, y err {err:.3e}"
+          f" (vs unrounded float64 {err_x:.3e})", flush=True)
     assert err <= TOL[w.dtype], err
