@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -209,6 +210,47 @@ def copy_bandwidth(gib, reps=5):
     del src, dst
     torch.cuda.empty_cache()
     return {"bytes_per_copy": 2 * n, "gbs": 2 * n / sec / 1e9, "us": sec * 1e6}
+
+
+def read_ceiling(gib, grids=(1024, 2048, 4096), reps=5):
+    """HBM read rate of a plain streaming-read kernel (hbm_read_probe.hip,
+    16-byte loads, one pass over `gib` GiB): the practical ceiling for the
+    read-dominated expert GEMMs, beside the datasheet peak.  Best grid, median
+    of `reps` timed passes after one untimed pass."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "combine_router_top_amd", "libhbm_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    n = int(gib * (1 << 30)) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    best = None
+    for g in grids:
+        ts = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rc = lib.hbm_read_probe(src.data_ptr(), n // 16, sink.data_ptr(), g, st.cuda_stream)
+            e1.record(st)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"hbm_read_probe failed: hipError {rc}")
+            if r:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        sec = statistics.median(ts)
+        if best is None or sec < best["us"] / 1e6:
+            best = {"bytes": n, "gbs": n / sec / 1e9, "us": sec * 1e6, "grid": g}
+    del src, sink
+    torch.cuda.empty_cache()
+    best["frac_of_peak"] = best["gbs"] / (HBM_PEAK / 1e9)
+    return best
 
 
 def cpu_baseline(w, inp, budget):
@@ -474,6 +516,7 @@ def main():
 
     torch.cuda.set_device(0)
     copy = copy_bandwidth(a.copy_gib) if a.copy_gib > 0 else None
+    rd = read_ceiling(a.copy_gib) if a.copy_gib > 0 else None
     d = {k: dev(v) for k, v in inp.items()}
     p = M.Spec.of(w, M.MOE_F_OVERLAP if a.overlap else 0)
     stream = torch.cuda.current_stream()
@@ -587,6 +630,8 @@ def main():
     roof["traffic"] = committed_traffic(w.name)
     roof["algorithmic_bytes"] = model["expert_gemm"]["bytes"]
     roof["algorithmic_flops"] = model["expert_gemm"]["flops"]
+    if rd and roof["unit"] == "GB/s":
+        roof["frac_of_read_ceiling"] = roof["achieved"] / rd["gbs"]
 
     out = {
         "metric": METRIC,
@@ -611,6 +656,7 @@ def main():
         "step_stats": step_stats,
         "wall_ms_per_step": wall / a.steps * 1e3,
         "hbm_copy": copy,
+        "hbm_read": rd,
         "env": run_env(),
         "input_gen_s": gen_s,
     }

@@ -22,6 +22,9 @@ LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "tile_forward.hip", "moe_api.cpp"]
+# measurement-only streaming-read probe, linked into a library of its own
+PROBE_SOURCE = "hbm_read_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libhbm_probe.so")
 
 
 def hipcc() -> str:
@@ -61,18 +64,25 @@ def build(jobs: int = 8, verbose: bool = True, defs=(), lib: str = LIB,
     """Compile and link.  ``defs`` are extra preprocessor definitions (tile-shape
     tuning knobs such as MOE_XG_NW=4); ``lib``/``build_dir`` redirect the output."""
     os.makedirs(build_dir, exist_ok=True)
+    with_probe = lib == LIB
+    srcs = SOURCES + ([PROBE_SOURCE] if with_probe else [])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: compile_one(s, defs, build_dir), SOURCES))
-    LIB_OUT = lib
-    tmp = LIB_OUT + ".tmp"
+        objs = dict(zip(srcs, ex.map(lambda s: compile_one(s, defs, build_dir), srcs)))
+    _link([objs[s] for s in SOURCES], lib, verbose)
+    if with_probe:
+        _link([objs[PROBE_SOURCE]], PROBE_LIB, verbose)
+    return lib
+
+
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB_OUT}")
-    return LIB_OUT
+        print(f"built {out}")
 
 
 def main():
