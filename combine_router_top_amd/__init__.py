@@ -398,5 +398,5 @@ def layer(p: Spec, x, w_gate, bias, w1, w3, w2, routing: bool = False, want_logi
     s2 = _stream(stream2) if (overlap and stream2 is not None) else None
     _check(lib().moe_layer(ctypes.byref(pc), _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(w1), _ptr(w3),
                            _ptr(w2), _ptr(y), ctypes.byref(ro) if ro is not None else None,
-                           _ptr(ws), ws.numel(), _stream(stream), s2))
+                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream), s2))
     return (y, r) if r is not None else y

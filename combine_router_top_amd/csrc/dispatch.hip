@@ -293,9 +293,26 @@ static int64_t n_chunks(const Prob& p) { return (p.tk() + DCH - 1) / DCH; }
 
 size_t dispatch_ws_bytes(const Prob& p) { return (size_t)n_chunks(p) * p.E * sizeof(int32_t); }
 
+// Empty batch: the histogram over all E experts and the local offsets are all
+// zero; one workgroup writes them (a kernel rather than a memset, so that the
+// call can be captured in a graph).
+__global__ __launch_bounds__(256) void clear_index_kernel(int32_t* __restrict__ counts_all, int E,
+                                                          int32_t* __restrict__ offsets, int n1) {
+  for (int i = threadIdx.x; i < E; i += 256) counts_all[i] = 0;
+  for (int i = threadIdx.x; i < n1; i += 256) offsets[i] = 0;
+}
+
+hipError_t launch_clear_index(const Prob& p, int32_t* counts_all, int32_t* offsets, hipStream_t st) {
+  if (!counts_all && !offsets) return hipSuccess;
+  hipLaunchKernelGGL(clear_index_kernel, dim3(1), dim3(256), 0, st, counts_all,
+                     counts_all ? p.E : 0, offsets, offsets ? p.n + 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
                                  hipStream_t st) {
+  if (p.tk() == 0) return launch_clear_index(p, counts_all, offsets, st);
   int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws);
   const int64_t nc = n_chunks(p);
   hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,

@@ -35,9 +35,10 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 moe_status_t check_problem(const moe_problem_t* p, moe::Prob* out) {
   if (!p) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
-  if (p->T <= 0 || p->d <= 0 || p->E <= 0 || p->k <= 0 || p->f <= 0)
-    return fail(MOE_ERR_INVALID_ARG, "T, d, E, k, f must be positive (T=%d d=%d E=%d k=%d f=%d)",
-                p->T, p->d, p->E, p->k, p->f);
+  if (p->T < 0 || p->d <= 0 || p->E <= 0 || p->k <= 0 || p->f <= 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "T must be >= 0 and d, E, k, f positive (T=%d d=%d E=%d k=%d f=%d)", p->T, p->d,
+                p->E, p->k, p->f);
   if (p->k > p->E) return fail(MOE_ERR_INVALID_ARG, "k=%d exceeds E=%d", p->k, p->E);
   if (p->n_local <= 0 || p->expert_lo < 0 || (int64_t)p->expert_lo + p->n_local > p->E)
     return fail(MOE_ERR_INVALID_ARG, "local experts [%d, %d+%d) not inside [0, %d)", p->expert_lo,
@@ -111,6 +112,7 @@ LayerWs layer_ws(const moe::Prob& p) {
 }
 
 size_t call_ws_bytes(const moe::Prob& p, int32_t call) {
+  if (p.T == 0) return 0;  // an empty batch launches no kernel that uses scratch
   switch (call) {
     case MOE_CALL_ROUTE: return moe::route_ws_bytes(p);
     case MOE_CALL_DISPATCH: return moe::dispatch_ws_bytes(p);
@@ -210,12 +212,13 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate
   moe::Prob q;
   moe_status_t st = check_problem(p, &q);
   if (st != MOE_OK) return st;
-  NEED_PTR(x);
   NEED_PTR(w_gate);
+  NEED_ALIGNED(w_gate);
+  if (q.T == 0) return ok();  // empty batch: nothing to route
+  NEED_PTR(x);
   NEED_PTR(topk_idx);
   NEED_PTR(topk_w);
   NEED_ALIGNED(x);
-  NEED_ALIGNED(w_gate);
   if ((st = check_ws(q, MOE_CALL_ROUTE, workspace, workspace_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return hip_status(moe::launch_route(q, x, w_gate, bias, logits, topk_idx, topk_w, workspace,
@@ -229,10 +232,15 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, const
   moe::Prob q;
   moe_status_t st = check_problem(p, &q);
   if (st != MOE_OK) return st;
-  NEED_PTR(topk_idx);
-  NEED_PTR(x);
   NEED_PTR(counts_all);
   NEED_PTR(offsets);
+  if (q.T == 0) {  // empty batch: all counts and offsets are zero
+    (void)hipGetLastError();
+    return hip_status(moe::launch_clear_index(q, counts_all, offsets, (hipStream_t)stream),
+                      "moe_dispatch");
+  }
+  NEED_PTR(topk_idx);
+  NEED_PTR(x);
   NEED_PTR(perm);
   NEED_PTR(inv);
   NEED_PTR(x_packed);
@@ -253,17 +261,18 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const
   moe::Prob q;
   moe_status_t st = check_problem(p, &q);
   if (st != MOE_OK) return st;
-  NEED_PTR(x_packed);
   NEED_PTR(offsets);
   NEED_PTR(w1);
   NEED_PTR(w3);
   NEED_PTR(w2);
-  NEED_PTR(h);
-  NEED_PTR(y_packed);
-  NEED_ALIGNED(x_packed);
   NEED_ALIGNED(w1);
   NEED_ALIGNED(w3);
   NEED_ALIGNED(w2);
+  if (q.T == 0) return ok();  // empty batch: no rows
+  NEED_PTR(x_packed);
+  NEED_PTR(h);
+  NEED_PTR(y_packed);
+  NEED_ALIGNED(x_packed);
   NEED_ALIGNED(h);
   NEED_ALIGNED(y_packed);
   if ((st = check_ws(q, MOE_CALL_EXPERT_GEMM, workspace, workspace_bytes)) != MOE_OK) return st;
@@ -383,6 +392,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int
   moe::Prob q;
   moe_status_t st = check_problem(p, &q);
   if (st != MOE_OK) return st;
+  if (q.T == 0) return ok();  // empty batch: no output rows
   NEED_PTR(y_packed);
   NEED_PTR(inv);
   NEED_PTR(topk_w);
@@ -401,17 +411,24 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   moe::Prob q;
   moe_status_t st = check_problem(p, &q);
   if (st != MOE_OK) return st;
-  NEED_PTR(x);
   NEED_PTR(w_gate);
   NEED_PTR(w1);
   NEED_PTR(w3);
   NEED_PTR(w2);
-  NEED_PTR(y);
-  NEED_ALIGNED(x);
   NEED_ALIGNED(w_gate);
   NEED_ALIGNED(w1);
   NEED_ALIGNED(w3);
   NEED_ALIGNED(w2);
+  if (q.T == 0) {  // empty batch: only the caller's counts and offsets are written (zeros)
+    (void)hipGetLastError();
+    return hip_status(moe::launch_clear_index(q, routing_out ? routing_out->counts_all : nullptr,
+                                              routing_out ? routing_out->offsets : nullptr,
+                                              (hipStream_t)stream),
+                      "moe_layer");
+  }
+  NEED_PTR(x);
+  NEED_PTR(y);
+  NEED_ALIGNED(x);
   NEED_ALIGNED(y);
   if ((q.flags & MOE_F_WRITE_LOGITS) && !(routing_out && routing_out->logits))
     return fail(MOE_ERR_INVALID_ARG, "MOE_F_WRITE_LOGITS needs routing_out->logits");

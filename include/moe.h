@@ -57,7 +57,7 @@ extern "C" {
 typedef int32_t moe_status_t;
 enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, k > E, bad expert range */
+  MOE_ERR_INVALID_ARG = 1, /* NULL pointer, negative T or non-positive d/E/k/f, k > E, bad expert range */
   MOE_ERR_UNSUPPORTED = 2, /* d or f not a multiple of 8, k > 32, E > 1024, bad dtype, misaligned */
   MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = 4          /* a HIP launch/runtime call failed; message in moe_last_error() */
@@ -85,7 +85,12 @@ enum {
 
 /*
  * Problem description.
- *   T          tokens (rows of x)
+ *   T          tokens (rows of x), >= 0.  T = 0 is an empty batch (a GPU that
+ *              received no tokens): the calls launch nothing but one small
+ *              kernel that writes zeros to counts_all and offsets where the
+ *              call has them; pointers to arrays with a T-sized dimension may
+ *              be NULL, every workspace size is 0, and the padded calls reject
+ *              it (their capacity must lie in 1 .. T).
  *   d          hidden size
  *   E          routed experts in total (1..1024)
  *   k          experts per token (1..min(E, 32))

@@ -467,6 +467,20 @@ def pin_token_outputs_unrounded(O):
             assert np.allclose(u, r, rtol=2.0 ** -5, atol=2.0 ** -5 * np.abs(u).max())
 
 
+def pin_empty_batch(O):
+    """T = 0: no assignments, so every count and offset is zero and every
+    T-sized output is empty (the degenerate batch of a GPU that received no
+    tokens)."""
+    for dtype in ("f32", "bf16"):
+        p, inp = _small_layer(O, dtype, T=0)
+        o = O.moe_layer(p, inp)
+        assert np.array_equal(o["counts_all"], np.zeros(p.E, dtype=np.int32))
+        assert np.array_equal(o["offsets"], np.zeros(p.n_local + 1, dtype=np.int32))
+        for key, shape in (("topk_idx", (0, p.k)), ("topk_w", (0, p.k)), ("perm", (0,)),
+                           ("inv", (0,)), ("y", (0, p.d))):
+            assert np.asarray(o[key]).shape == shape, key
+
+
 def pin_layer_padded(O):
     """The padded layer against the unpadded one: with C = the largest local
     count the outputs agree; with a smaller C they agree with the unpadded

@@ -54,7 +54,7 @@ def _route(p, x=FAKE, wg=FAKE, idx=FAKE, w=FAKE, ws=FAKE, wsb=1 << 30):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(T=0), M.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), M.MOE_ERR_INVALID_ARG),
     (dict(d=-8), M.MOE_ERR_INVALID_ARG),
     (dict(k=9), M.MOE_ERR_INVALID_ARG),            # k > E
     (dict(k=0), M.MOE_ERR_INVALID_ARG),
@@ -92,6 +92,30 @@ def test_null_and_misaligned_pointers():
                              None) == M.MOE_ERR_INVALID_ARG
     assert L.moe_dispatch(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30,
                           None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_empty_batch_host():
+    """T = 0 is a valid empty batch: no workspace, T-sized pointers may be
+    NULL, and route / expert GEMM / combine return at once (nothing to launch;
+    dispatch and the layer clear counts and offsets, covered on the GPU).  The
+    weights are still checked; the padded calls reject T = 0 (no capacity in
+    1 .. T)."""
+    L = M.lib()
+    p = _p(T=0)
+    for call in range(M.MOE_CALL_ROUTE, M.MOE_CALL_EXPERT_GEMM_PADDED + 1):
+        assert L.moe_workspace_bytes(ctypes.byref(p), call) == 0
+        assert L.moe_last_error() == b""
+    assert _route(p, x=0, idx=0, w=0, ws=0, wsb=0) == M.MOE_OK
+    assert _route(p, x=0, wg=0, idx=0, w=0, ws=0, wsb=0) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_gemm(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, 0, 0, None, 0, None) == M.MOE_OK
+    assert L.moe_expert_gemm(ctypes.byref(p), 0, FAKE, FAKE, FAKE, 0, 0, 0, None, 0, None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(p), 0, 0, 0, 0, None) == M.MOE_OK
+    assert L.moe_dispatch(ctypes.byref(p), 0, 0, 0, FAKE, 0, 0, 0, None, 0, None) == \
+        M.MOE_ERR_INVALID_ARG                                    # counts_all is still required
+    assert L.moe_dispatch_padded(ctypes.byref(p), 1, 0, 0, FAKE, FAKE, 0, 0, 0, None, 0, None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert b"capacity" in L.moe_last_error()
 
 
 def test_workspace_checks():

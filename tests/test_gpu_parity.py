@@ -299,3 +299,43 @@ def test_layer_no_local_tokens():
     assert int(host(r["offsets"])[-1]) == 0
     assert np.all(host(r["inv"]) == -1)
     assert not np.any(host(y))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_batch(dtype):
+    """T = 0 (a GPU that received no tokens): every call succeeds with empty
+    outputs, no workspace, and dispatch and the layer write zero counts and
+    offsets over what was there; the oracle gives the same."""
+    import torch
+    w = W("empty", 0, 64, 16, 2, 32, 4, 8, dtype, seed=26)
+    inp = workloads.generate(w)
+    ref = O.moe_layer(w, inp)
+    p = M.Spec.of(w)
+    for call in range(M.MOE_CALL_ROUTE, M.MOE_CALL_EXPERT_GEMM_PADDED + 1):
+        assert M.workspace_bytes(p, call) == 0
+    x, wg = dev(inp["x"]), dev(inp["w_gate"])
+    w1, w3, w2 = dev(inp["w1"]), dev(inp["w3"]), dev(inp["w2"])
+    idx, tw, logits = M.route(p, x, wg, want_logits=True)
+    assert idx.shape == (0, w.k) and tw.shape == (0, w.k) and logits.shape == (0, w.E)
+    stale = {
+        "counts_all": torch.full((w.E,), -5, dtype=torch.int32, device="cuda"),
+        "offsets": torch.full((w.n_local + 1,), -5, dtype=torch.int32, device="cuda"),
+        "perm": torch.empty(0, dtype=torch.int32, device="cuda"),
+        "inv": torch.empty(0, dtype=torch.int32, device="cuda"),
+        "x_packed": torch.empty((0, w.d), dtype=x.dtype, device="cuda"),
+    }
+    o = M.dispatch(p, idx, x, out=stale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o["counts_all"]), ref["counts_all"])
+    assert np.array_equal(host(o["offsets"]), ref["offsets"])
+    h, yp = M.expert_gemm(p, o["x_packed"], o["offsets"], w1, w3, w2)
+    y = M.combine(p, yp, o["inv"], tw)
+    assert h.shape == (0, w.f) and yp.shape == (0, w.d) and y.shape == (0, w.d)
+    y2, r = M.layer(p, x, wg, None, w1, w3, w2, routing=True)
+    torch.cuda.synchronize()
+    assert y2.shape == (0, w.d)
+    assert np.array_equal(host(r["counts_all"]), ref["counts_all"])
+    assert np.array_equal(host(r["offsets"]), ref["offsets"])
+    with pytest.raises(M.MoeError):
+        M.dispatch_padded(p, 1, idx, x)
+
