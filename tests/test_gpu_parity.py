@@ -58,6 +58,11 @@ SMALL = {
     # top-k with 2 (96 experts) and 8 (384 experts) values per lane
     "topk_e96": W("topk_e96", 130, 64, 96, 6, 32, 0, 16, "bf16", seed=24),
     "topk_e384": W("topk_e384", 70, 128, 384, 8, 32, 16, 32, "bf16", seed=25),
+    # the largest E (16 values per lane in top-k, four 256-expert router
+    # blocks) and, with it, the largest k on 1024 local experts: over a
+    # thousand segments of 0..5 rows through the grouped GEMM schedule
+    "topk_e1024": W("topk_e1024", 64, 64, 1024, 8, 32, 100, 16, "bf16", seed=27),
+    "max_e1024_k32": W("max_e1024_k32", 48, 64, 1024, 32, 32, 0, 1024, "bf16", seed=28),
     # thin down-projection blocks of 448 and 384 output columns (the width
     # that fills the last round: 32 x 16 and 16 x 16 blocks)
     "thin_tcols448": W("thin_tcols448", 64, 7168, 32, 2, 64, 0, 32, "bf16", seed=26),
@@ -90,7 +95,7 @@ def test_route(name):
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
                                   "wide_ksplit", "wide_e20", "topk_e96",
-                                  "topk_e384"])
+                                  "topk_e384", "topk_e1024"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
