@@ -7,9 +7,11 @@
 //
 // Kernels
 //   router_wide_mfma    bf16, E % 4 == 0 and E > 16: split-K MFMA GEMM on the
-//                       pipelined core (gemm_core.h); 8 waves, each 160
-//                       tokens x 32 experts, the workgroup 160 x 256.  Writes
-//                       fp32 partial sums per K split.
+//                       pipelined core (gemm_core.h); 8 waves, each 16 MT
+//                       tokens x 32 experts, the workgroup 16 MT x 256 with
+//                       MT = 10, or 5 when the 160-token grid would fill less
+//                       than half the chip (short batches).  Writes fp32
+//                       partial sums per K split.
 //   router_narrow_mfma  bf16, E <= 16 and E*d <= 32K: W_g^T staged once in LDS,
 //                       each wave streams its own 32 token rows with buffer
 //                       loads straight into MFMA A fragments, one 128-K chunk
@@ -30,18 +32,23 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // wide router (bf16, MFMA, split-K) on the pipelined core of gemm_core.h
 // ---------------------------------------------------------------------------
-// 160 tokens x 256 experts per workgroup (8 waves, each 160 x 32), so that the
-// gate matrix is re-read once per 160 tokens; K is split to fill the chip.
+// 16 MT tokens x 256 experts per workgroup (8 waves, each 16 MT x 32), so
+// that the gate matrix is re-read once per 16 MT tokens; K is split to fill
+// the chip.  MT = 10 for long batches; a short batch (decode) has too few
+// token blocks to fill the chip even with the deepest splits, and halving the
+// block doubles its workgroups.
 constexpr int RW_NW = 8;
 constexpr int RW_CPL = 2;
-constexpr int RW_MT = 10;          // m-tiles per workgroup
-constexpr int RW_BM = 16 * RW_MT;  // tokens per workgroup
+constexpr int RW_MT_LONG = 10;     // m-tiles per workgroup
+constexpr int RW_MT_SHORT = 5;
 constexpr int RW_BN = 256;         // experts per workgroup (8 waves x 32)
 
+template <int RW_MT>
 __global__ __launch_bounds__(64 * RW_NW) void router_wide_mfma(const bf16_t* __restrict__ x,
                                                                const bf16_t* __restrict__ wg,
                                                                float* __restrict__ part, int T,
                                                                int d, int E, int kchunk) {
+  constexpr int RW_BM = 16 * RW_MT;  // tokens per workgroup
   __shared__ __attribute__((aligned(16))) bf16_t As[gc_lds_elems<RW_NW, RW_CPL, RW_MT>()];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, g = lane >> 4;
@@ -343,16 +350,27 @@ static RouteKind route_kind(const Prob& p) {
   return ROUTE_PLAIN;
 }
 
-static int route_splits(const Prob& p) {
-  if (route_kind(p) != ROUTE_WIDE) return 1;
+static int64_t rw_blocks(const Prob& p, int mt) {
+  return (int64_t)((p.T + 16 * mt - 1) / (16 * mt)) * ((p.E + RW_BN - 1) / RW_BN);
+}
+
+static int rw_splits(const Prob& p, int mt) {
   // at most one workgroup per compute unit (a second round of a few
   // workgroups would double the time), every split keeps >= 256 of K
-  const int64_t blocks = (int64_t)((p.T + RW_BM - 1) / RW_BM) * ((p.E + RW_BN - 1) / RW_BN);
-  int64_t s = 256 / blocks;
+  int64_t s = 256 / rw_blocks(p, mt);
   if (s < 1) s = 1;
   const int64_t smax = p.d / 256 > 1 ? p.d / 256 : 1;
   if (s > smax) s = smax;
   return (int)s;
+}
+
+// 160-token blocks when their grid fills at least half the chip, else 80
+static int route_mt(const Prob& p) {
+  return rw_blocks(p, RW_MT_LONG) * rw_splits(p, RW_MT_LONG) >= 128 ? RW_MT_LONG : RW_MT_SHORT;
+}
+
+static int route_splits(const Prob& p) {
+  return route_kind(p) == ROUTE_WIDE ? rw_splits(p, route_mt(p)) : 1;
 }
 
 static int route_kchunk(const Prob& p, int S) {
@@ -372,9 +390,11 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
   const int S = route_splits(p);
   if (kind == ROUTE_WIDE) {
     const int kchunk = route_kchunk(p, S);
-    dim3 grid((p.T + RW_BM - 1) / RW_BM, S, (p.E + RW_BN - 1) / RW_BN);
-    hipLaunchKernelGGL(router_wide_mfma, grid, dim3(64 * RW_NW), 0, st, (const bf16_t*)x, (const bf16_t*)wg, part, p.T,
-                       p.d, p.E, kchunk);
+    const int mt = route_mt(p);
+    dim3 grid((p.T + 16 * mt - 1) / (16 * mt), S, (p.E + RW_BN - 1) / RW_BN);
+    auto kern = mt == RW_MT_LONG ? router_wide_mfma<RW_MT_LONG> : router_wide_mfma<RW_MT_SHORT>;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * RW_NW), 0, st, (const bf16_t*)x, (const bf16_t*)wg,
+                       part, p.T, p.d, p.E, kchunk);
   } else if (kind == ROUTE_NARROW) {
     dim3 grid((p.T + RN_ROWS - 1) / RN_ROWS);
     const size_t lds = (size_t)p.E * p.d * sizeof(bf16_t);

@@ -62,6 +62,9 @@ SMALL = {
     # blocks) and, with it, the largest k on 1024 local experts: over a
     # thousand segments of 0..5 rows through the grouped GEMM schedule
     "topk_e1024": W("topk_e1024", 64, 64, 1024, 8, 32, 100, 16, "bf16", seed=27),
+    # enough token blocks for the 160-token router tile (17 blocks x 8 K
+    # splits of 320; the 7th is 184 deep, the 8th empty), ragged token tail
+    "router_long": W("router_long", 2600, 2104, 32, 4, 64, 8, 8, "bf16", seed=29),
     "max_e1024_k32": W("max_e1024_k32", 48, 64, 1024, 32, 32, 0, 1024, "bf16", seed=28),
     # thin down-projection blocks of 448 and 384 output columns (the width
     # that fills the last round: 32 x 16 and 16 x 16 blocks)
@@ -95,7 +98,7 @@ def test_route(name):
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
                                   "wide_ksplit", "wide_e20", "topk_e96",
-                                  "topk_e384", "topk_e1024"])
+                                  "topk_e384", "topk_e1024", "router_long"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
