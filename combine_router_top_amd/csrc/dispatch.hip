@@ -18,6 +18,8 @@
 //                      prefix in LDS, and inside a wave the rank among equal
 //                      experts from ballots over the expert-id bits.
 //   gather_rows_kernel one wave per packed row, 16-byte vector copies.
+// A batch of at most 1024 assignments (one chunk, e.g. decode) launches only
+// the scatter kernel, whose single workgroup builds the histogram itself.
 #include <algorithm>
 
 #include "common.h"
@@ -67,6 +69,9 @@ __device__ __forceinline__ int block_excl_scan_256(int v, int* lds4, int* tot) {
   return wbase + x - v;
 }
 
+// ONE: the whole batch is one chunk (T k <= 1024) and this single workgroup
+// builds the histogram itself in LDS, so chunk_hist_kernel is not launched.
+template <bool ONE>
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ idx, int64_t TK,
                                                       int E, int lo, int n, int nchunks,
                                                       const int32_t* __restrict__ chunk_hist,
@@ -77,14 +82,30 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   __shared__ int base[DMAXE];
   __shared__ int wpos[4][DMAXE];
   __shared__ int scan_tmp[4];
+  __shared__ int hl[ONE ? DMAXE : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
+
+  if constexpr (ONE) {
+    for (int e = tid; e < E; e += 256) hl[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < DCH / 256; ++q) {
+      const int64_t a = q * 256 + tid;
+      if (a < TK) {
+        const int e = idx[a];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hl[e], 1);
+      }
+    }
+    __syncthreads();
+  }
 
   // 1. per local expert: total count and count in the chunks before this one
   // (DUN independent loads in flight per round instead of one round trip per chunk)
   for (int e = tid; e < n; e += 256) {
     int tot = 0, pre = 0;
-    int cc = 0;
+    int cc = ONE ? nchunks : 0;
+    if constexpr (ONE) tot = hl[lo + e];
     for (; cc + DUN <= nchunks; cc += DUN) {
       int v[DUN];
 #pragma unroll
@@ -128,7 +149,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     if (tid == 0) offsets[n] = total;
     for (int e = tid; e < E; e += 256) {
       int t = 0;
-      int cc = 0;
+      int cc = ONE ? nchunks : 0;
+      if constexpr (ONE) t = hl[e];
       for (; cc + DUN <= nchunks; cc += DUN) {
         int v[DUN];
 #pragma unroll
@@ -315,12 +337,17 @@ hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* cou
   if (p.tk() == 0) return launch_clear_index(p, counts_all, offsets, st);
   int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws);
   const int64_t nc = n_chunks(p);
+  if (nc == 1) {  // one workgroup does it all
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3(1), dim3(256), 0, st, idx, p.tk(), p.E, p.lo,
+                       p.n, 1, (const int32_t*)nullptr, counts_all, offsets, perm, inv);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
                      chunk_hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E, p.lo,
-                     p.n, (int)nc, chunk_hist, counts_all, offsets, perm, inv);
+  hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
+                     p.lo, p.n, (int)nc, chunk_hist, counts_all, offsets, perm, inv);
   return hipGetLastError();
 }
 
