@@ -18,6 +18,9 @@
 //                       in flight.  HBM-bound on x.
 //   router_plain        any dtype/shape: one thread per logit (fp32 problems
 //                       and shapes the MFMA kernels do not cover).
+//   topk_softmax_multi  12 or more K splits (short batches): one workgroup
+//                       per token, 4 waves each sum a quarter of the splits,
+//                       quarters added in wave order, wave 0 selects.
 //   topk_softmax_kernel one wave per token: sums the K splits in fixed order
 //                       (loads of 8 splits x all of a lane's experts in
 //                       flight together), adds the bias, optionally stores
@@ -262,43 +265,14 @@ __device__ __forceinline__ float key_to_f32(uint32_t ok) {
 }
 
 // NV = values per lane = ceil(E / 64).
+// Bias, optional logit store, k rounds of a wave-wide max over (value, index)
+// keys and the softmax over the k selected: one wave, token t, with the
+// lane's summed logits v[j] of experts lane + 64 j.
 template <int NV>
-__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ part,
-                                                           int nsplit, const float* __restrict__ bias,
-                                                           float* __restrict__ logits_out, int T,
-                                                           int E, int k, int32_t* __restrict__ idx,
-                                                           float* __restrict__ w) {
+__device__ __forceinline__ void topk_select(const float (&v)[NV], const float* __restrict__ bias,
+                                            float* __restrict__ logits_out, int t, int E, int k,
+                                            int32_t* __restrict__ idx, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  // sum each expert's K splits in ascending order; the loads of 8 splits of
-  // all NV experts of the lane are issued together (one round trip per 8
-  // splits, not per expert and 8 splits)
-  const int64_t sstride = (int64_t)T * E;
-  const float* pt = part + (int64_t)t * E + lane;
-  float v[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = lane + 64 * j < E ? pt[64 * j] : 0.f;
-  int s = 1;
-  for (; s + 8 <= nsplit; s += 8) {
-    float q[NV][8];
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        q[j][u] = lane + 64 * j < E ? pt[(int64_t)(s + u) * sstride + 64 * j] : 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[j] += q[j][u];
-  }
-  for (; s < nsplit; ++s) {
-    float q[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) q[j] = lane + 64 * j < E ? pt[(int64_t)s * sstride + 64 * j] : 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] += q[j];
-  }
   uint64_t key[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
@@ -337,6 +311,90 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     idx[(int64_t)t * k + lane] = mye;
     w[(int64_t)t * k + lane] = ex / sum;
   }
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ part,
+                                                           int nsplit, const float* __restrict__ bias,
+                                                           float* __restrict__ logits_out, int T,
+                                                           int E, int k, int32_t* __restrict__ idx,
+                                                           float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  // sum each expert's K splits in ascending order; the loads of 8 splits of
+  // all NV experts of the lane are issued together (one round trip per 8
+  // splits, not per expert and 8 splits)
+  const int64_t sstride = (int64_t)T * E;
+  const float* pt = part + (int64_t)t * E + lane;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = lane + 64 * j < E ? pt[64 * j] : 0.f;
+  int s = 1;
+  for (; s + 8 <= nsplit; s += 8) {
+    float q[NV][8];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        q[j][u] = lane + 64 * j < E ? pt[(int64_t)(s + u) * sstride + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[j] += q[j][u];
+  }
+  for (; s < nsplit; ++s) {
+    float q[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) q[j] = lane + 64 * j < E ? pt[(int64_t)s * sstride + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] += q[j];
+  }
+  topk_select<NV>(v, bias, logits_out, t, E, k, idx, w);
+}
+
+// Deep K splits (short batches): one workgroup per token, each of its 4 waves
+// sums a contiguous quarter of the splits (loads of up to 8 splits in flight
+// together), the quarters are added in wave order through LDS, and wave 0
+// selects.
+constexpr int TK_MULTI_MIN_SPLITS = 12;
+
+template <int NV>
+__global__ __launch_bounds__(256) void topk_softmax_multi(const float* __restrict__ part,
+                                                          int nsplit, const float* __restrict__ bias,
+                                                          float* __restrict__ logits_out, int T,
+                                                          int E, int k, int32_t* __restrict__ idx,
+                                                          float* __restrict__ w) {
+  __shared__ float red[4][NV * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int s0 = wave * nsplit / 4, s1 = (wave + 1) * nsplit / 4;
+  const int64_t sstride = (int64_t)T * E;
+  const float* pt = part + (int64_t)t * E + lane;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = 0.f;
+  for (int s = s0; s < s1; s += 8) {
+    float q[NV][8];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        q[j][u] = (s + u < s1 && lane + 64 * j < E) ? pt[(int64_t)(s + u) * sstride + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[j] += q[j][u];
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) red[wave][64 * j + lane] = v[j];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    v[j] = ((red[0][64 * j + lane] + red[1][64 * j + lane]) + red[2][64 * j + lane]) +
+           red[3][64 * j + lane];
+  topk_select<NV>(v, bias, logits_out, t, E, k, idx, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,6 +471,16 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nv = (p.E + 63) / 64;
+  if (S >= TK_MULTI_MIN_SPLITS) {
+    auto tk = nv <= 1 ? topk_softmax_multi<1>
+            : nv <= 2 ? topk_softmax_multi<2>
+            : nv <= 4 ? topk_softmax_multi<4>
+            : nv <= 8 ? topk_softmax_multi<8>
+                      : topk_softmax_multi<16>;
+    hipLaunchKernelGGL(tk, dim3(p.T), dim3(256), 0, st, part, S, bias, logits, p.T, p.E, p.k, idx,
+                       w);
+    return hipGetLastError();
+  }
   auto tk = nv <= 1 ? topk_softmax_kernel<1>
           : nv <= 2 ? topk_softmax_kernel<2>
           : nv <= 4 ? topk_softmax_kernel<4>

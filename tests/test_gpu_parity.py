@@ -65,6 +65,9 @@ SMALL = {
     # enough token blocks for the 160-token router tile (17 blocks x 8 K
     # splits of 320; the 7th is 184 deep, the 8th empty), ragged token tail
     "router_long": W("router_long", 2600, 2104, 32, 4, 64, 8, 8, "bf16", seed=29),
+    # deep K splits (16 and 12): top-k sums them in four waves per token
+    "topk_deep_e256": W("topk_deep_e256", 40, 4096, 256, 8, 32, 32, 32, "bf16", seed=30),
+    "topk_deep_e1024": W("topk_deep_e1024", 20, 3072, 1024, 8, 32, 512, 16, "bf16", seed=31),
     "max_e1024_k32": W("max_e1024_k32", 48, 64, 1024, 32, 32, 0, 1024, "bf16", seed=28),
     # thin down-projection blocks of 448 and 384 output columns (the width
     # that fills the last round: 32 x 16 and 16 x 16 blocks)
@@ -98,7 +101,8 @@ def test_route(name):
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
                                   "wide_ksplit", "wide_e20", "topk_e96",
-                                  "topk_e384", "topk_e1024", "router_long"])
+                                  "topk_e384", "topk_e1024", "router_long", "topk_deep_e256",
+                                  "topk_deep_e1024"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
