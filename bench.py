@@ -17,7 +17,7 @@ Prints one JSON line:
   phases        every ABI call timed the same way, with its own roofline
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
 
-This build runs on one GPU only; --gpus above 1 exits with a message.
+It measures one GPU; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
@@ -490,7 +490,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {a.gpus}, "
+        print(f"bench.py: measures one GPU only (asked for --gpus {a.gpus}, "
               f"WORLD_SIZE {world}); the layer's expert-parallel sharding is a design note, "
               f"not built", file=sys.stderr)
         sys.exit(2)
