@@ -36,8 +36,11 @@
  *     device or the host.
  *   - Validation is host-side and shape-only.  On error nothing is launched,
  *     a status is returned and moe_last_error() describes it.  Data-dependent
- *     conditions are not checked: NaN/Inf inputs and expert indices outside
- *     [0, E) in a caller-supplied topk_idx are undefined behaviour.
+ *     conditions are not checked: NaN/Inf inputs, expert indices outside
+ *     [0, E) in a caller-supplied topk_idx, and a topk_idx row that names the
+ *     same expert twice are undefined behaviour (the buffers sized from
+ *     rows_max hold T*min(k, n_local) rows only because the k experts of a
+ *     token are distinct, as moe_route produces them).
  *   - Results are bitwise deterministic for identical inputs and launch
  *     configuration (no floating-point atomics).
  *   - The calls are re-entrant; concurrent calls must not share workspace.
@@ -155,7 +158,9 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_gate
 /*
  * Dispatch (CUCo, Table 4, "MoE Dispatch/Combine": variable-size per-peer
  * transfers with no padding).  Assignment a = t*k + j is local when
- * expert_lo <= topk_idx[a] < expert_lo + n_local.
+ * expert_lo <= topk_idx[a] < expert_lo + n_local.  The k entries of a row of
+ * topk_idx must be distinct experts in [0, E) (then A <= rows_max); anything
+ * else is undefined behaviour and is not detected.
  *   counts_all [E]          counts_all[e] = #assignments to expert e (all E)
  *   offsets    [n_local+1]  offsets[0] = 0, offsets[e+1] = offsets[e] + counts_all[expert_lo+e]
  *   perm       [rows_max]   perm[p] = a, local assignments sorted by local expert,

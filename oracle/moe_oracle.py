@@ -54,6 +54,7 @@ __all__ = [
     "gather_rows_padded",
     "silu",
     "swiglu_experts",
+    "down_projection",
     "combine",
     "moe_layer",
     "moe_layer_padded",
@@ -261,14 +262,53 @@ def swiglu_experts(x_packed: np.ndarray, offsets: np.ndarray, w1, w3, w2, dtype:
     return h, yp
 
 
+def down_projection(h: np.ndarray, offsets: np.ndarray, w2, dtype: str,
+                    row_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """The second half of step 7 on its own: y_packed[R_e] = rnd(h[R_e] W2_e)
+    for float64 values h (on the storage grid), per local expert segment.
+
+    With ``row_scale`` (one float64 factor per packed row), each row's exact
+    product is multiplied by its factor before the one rounding:
+    y_packed[p] = rnd(s[p] * (h[p] W2_e)).  This is the layout in which the
+    gate weight of a row's assignment is applied in the down projection's
+    epilogue instead of in combine (the pages name the sequential
+    dispatch/compute/combine phases as the MoE bottleneck, CUCo Table 4, row
+    "MoE Dispatch/Combine"; folding the weight into the expert output lets
+    combine be a plain sum)."""
+    h = np.asarray(h, dtype=np.float64)
+    n_local = len(offsets) - 1
+    d = np.asarray(w2).shape[2]
+    yp = np.zeros((h.shape[0], d), dtype=np.float64)
+    for e in range(n_local):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        prod = h[r0:r1] @ widen(w2[e], dtype)
+        if row_scale is not None:
+            prod = np.asarray(row_scale, dtype=np.float64)[r0:r1, None] * prod
+        yp[r0:r1] = rnd(prod, dtype)
+    return yp
+
+
 # ---------------------------------------------------------------------------
 # 8. combine
 # ---------------------------------------------------------------------------
-def combine(y_packed: np.ndarray, inv: np.ndarray, topk_w: np.ndarray, dtype: str) -> np.ndarray:
+def combine(y_packed: np.ndarray, inv: np.ndarray, topk_w: Optional[np.ndarray], dtype: str,
+            k: Optional[int] = None) -> np.ndarray:
     """y[t] = rnd(sum_j w[t,j] * y_packed[inv[t*k+j]]) over local slots, in slot
     order, float64; exact zero rows for tokens with no local slot.  This is the
-    pages' "combine" (CUCo, Table 4), un-permute plus weighted sum."""
-    W = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    pages' "combine" (CUCo, Table 4), un-permute plus weighted sum.
+
+    ``topk_w=None`` is the plain sum of the local slots' rows (weights already
+    applied in the down projection, see ``down_projection``); then ``k`` gives
+    the slots per token."""
+    if topk_w is None:
+        if k is None:
+            raise ValueError("k is needed when topk_w is None")
+        T = np.asarray(inv).shape[0] // k
+        W = np.ones((T, k), dtype=np.float64)
+    else:
+        W = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
     T, k = W.shape
     inv2 = np.asarray(inv).reshape(T, k)
     d = y_packed.shape[1]
@@ -283,11 +323,16 @@ def combine(y_packed: np.ndarray, inv: np.ndarray, topk_w: np.ndarray, dtype: st
 # whole layer
 # ---------------------------------------------------------------------------
 def moe_layer(p, inputs: Dict[str, np.ndarray], routing: Optional[Dict[str, np.ndarray]] = None,
-              with_experts: bool = True) -> Dict[str, np.ndarray]:
+              with_experts: bool = True, fold_weight: bool = False) -> Dict[str, np.ndarray]:
     """Steps 1-8 for problem ``p`` (fields T, d, E, k, f, expert_lo, n_local,
     dtype).  If ``routing`` supplies topk_idx/topk_w (for instance the GPU's),
     steps 3-8 follow that routing instead of the oracle's own (so that a
-    legitimate near-tie flip in step 2 cannot cascade)."""
+    legitimate near-tie flip in step 2 cannot cascade).
+
+    ``fold_weight``: the gate weight of each packed row's assignment scales
+    that row in the down projection, before its rounding
+    (y_packed[p] = rnd(w[perm[p]] * (h[p] W2_e))), and combine sums the rows
+    unweighted.  It moves one rounding point; the exact result is the same."""
     out: Dict[str, np.ndarray] = {}
     L = router_logits(inputs["x"], inputs["w_gate"], p.dtype, inputs.get("bias"))
     out["logits"] = L
@@ -301,8 +346,15 @@ def moe_layer(p, inputs: Dict[str, np.ndarray], routing: Optional[Dict[str, np.n
     out["x_packed"] = xp
     if with_experts:
         h, yp = swiglu_experts(xp, offsets, inputs["w1"], inputs["w3"], inputs["w2"], p.dtype)
-        out["h"], out["y_packed"] = h, yp
-        out["y"] = combine(yp, inv, w, p.dtype)
+        if fold_weight:
+            wf = np.asarray(w, dtype=np.float32).astype(np.float64).ravel()
+            yp = down_projection(h, offsets, inputs["w2"], p.dtype,
+                                 row_scale=wf[np.asarray(perm, dtype=np.int64)])
+            out["h"], out["y_packed"] = h, yp
+            out["y"] = combine(yp, inv, None, p.dtype, k=p.k)
+        else:
+            out["h"], out["y_packed"] = h, yp
+            out["y"] = combine(yp, inv, w, p.dtype)
     return out
 
 

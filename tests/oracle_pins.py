@@ -373,6 +373,103 @@ def pin_hand_swiglu(O):
     assert np.allclose(y[0], [eval(s, {"exp": math.exp}) for s in g["y_formula"]], rtol=1e-15)
 
 
+def pin_down_projection_integer_exact(O):
+    """Integer-valued h and W2 (exact in bf16): every product sum is a small
+    integer, so y_packed equals numpy's int64 matmul exactly, per segment,
+    also with power-of-two row scales (exact in binary); an empty segment
+    writes nothing."""
+    rng = np.random.default_rng(41)
+    f, d, n = 24, 16, 3
+    offsets = np.array([0, 4, 4, 9], dtype=np.int32)
+    hi = rng.integers(-3, 4, size=(9, f))
+    w2i = rng.integers(-2, 3, size=(n, f, d))
+    store = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    scale = np.ldexp(1.0, rng.integers(-3, 2, size=9))
+    for dtype in ("bf16", "f32"):
+        w2 = store(w2i) if dtype == "bf16" else w2i.astype(np.float32)
+        for rs in (None, scale):
+            y = O.down_projection(hi.astype(np.float64), offsets, w2, dtype, row_scale=rs)
+            for e in range(n):
+                r0, r1 = offsets[e], offsets[e + 1]
+                ref = (hi[r0:r1] @ w2i[e]).astype(np.float64)
+                if rs is not None:
+                    ref = ref * rs[r0:r1, None]
+                assert np.array_equal(y[r0:r1], ref), (dtype, e)
+
+
+def pin_down_projection_brute_force(O):
+    """bf16 down projection with general row scales against scalar loops:
+    y[p][c] = rnd(s[p] * sum_j h[p][j] W2[j][c]), the scale applied to the
+    exact sum before the one rounding (scaling a rounded value would round
+    twice)."""
+    rng = np.random.default_rng(43)
+    f, d = 20, 12
+    offsets = np.array([0, 6], dtype=np.int32)
+    store = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    h = O.widen(store(rng.standard_normal((6, f))), "bf16")
+    w2 = store(rng.standard_normal((1, f, d)) / 4)
+    W2 = O.widen(w2[0], "bf16").tolist()
+    s = rng.uniform(0.05, 0.95, size=6)
+    y = O.down_projection(h, offsets, w2, "bf16", row_scale=s)
+    rb = lambda v: float(O.round_bf16(np.array([v]))[0])
+    H = h.tolist()
+    for p_ in range(6):
+        for c in range(d):
+            assert y[p_, c] == rb(s[p_] * math.fsum(H[p_][j] * W2[j][c] for j in range(f))), (p_, c)
+
+
+def pin_fold_weight(O):
+    """The gate weight folded into the down projection moves one rounding
+    point: (a) with power-of-two gate weights rnd(w Y) = w rnd(Y) exactly, so
+    the folded layer equals the weighted-combine layer bit for bit; (b) with
+    the real weights each output element stays within two bf16 steps of the
+    weighted-combine layer (one rounding moved per slot, plus the final one);
+    (c) a pure-Python walk of one token: y[c] = rnd(sum over local slots of
+    rnd(w_j (h_j W2_e)[c])) in slot order."""
+    p, inp = _small_layer(O, "bf16", T=40, d=16, E=8, k=3, f=24, lo=1, n=5)
+    base = O.moe_layer(p, inp)
+    pw = np.ldexp(1.0, -np.arange(1, p.k + 1)).astype(np.float32)
+    routing = {"topk_idx": base["topk_idx"], "topk_w": np.tile(pw, (p.T, 1))}
+    a = O.moe_layer(p, inp, routing=routing)
+    b = O.moe_layer(p, inp, routing=routing, fold_weight=True)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["h"], b["h"])
+    f = O.moe_layer(p, inp, fold_weight=True)
+    tol = 2.0 * 2.0 ** -7 * np.abs(base["y"]).max()
+    assert np.abs(f["y"] - base["y"]).max() <= tol
+    # (c) one token with two or more local slots, by hand
+    inv = f["inv"].reshape(p.T, p.k)
+    t = int(np.nonzero((inv >= 0).sum(1) >= 2)[0][0])
+    rb = lambda v: float(O.round_bf16(np.array([v]))[0])
+    X = O.widen(inp["x"], "bf16")[t]
+    out = [0.0] * p.d
+    for j in range(p.k):
+        e = int(f["topk_idx"][t, j]) - p.expert_lo
+        if not 0 <= e < p.n_local:
+            continue
+        W1, W3, W2 = (O.widen(inp[n_][e], "bf16") for n_ in ("w1", "w3", "w2"))
+        hrow = []
+        for q in range(p.f):
+            a1 = math.fsum(X[i] * W1[i, q] for i in range(p.d))
+            a3 = math.fsum(X[i] * W3[i, q] for i in range(p.d))
+            hrow.append(rb(a1 / (1.0 + math.exp(-a1)) * a3))
+        wj = float(f["topk_w"][t, j])
+        for c in range(p.d):
+            out[c] += rb(wj * math.fsum(hrow[q] * W2[q, c] for q in range(p.f)))
+    ref = np.array([rb(v) for v in out])
+    assert np.max(np.abs(f["y"][t] - ref)) <= 2.0 ** -7 * np.abs(ref).max(), t
+
+
+def pin_combine_unweighted(O):
+    """combine with no weights is the plain slot-order sum: equal to unit
+    weights."""
+    p, inp = _small_layer(O, "bf16")
+    o = O.moe_layer(p, inp, with_experts=False)
+    yp = O.widen(o["x_packed"], "bf16")
+    a = O.combine(yp, o["inv"], None, "bf16", k=p.k)
+    b = O.combine(yp, o["inv"], np.ones((p.T, p.k), dtype=np.float32), "bf16")
+    assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # combine and the whole layer
 # ---------------------------------------------------------------------------

@@ -4,9 +4,21 @@ times (one moe_layer call on the default stream).
 All tokens: logits within 1e-5; top-k equal to the oracle's top-k on the GPU's
 own logits; against the oracle's own logits only near-tie tokens may differ;
 counts, offsets, permutation and inverse bit-exact; tokens with no local slot
-give exact zero rows; two runs bitwise equal.
-Sampled tokens (the oracle evaluates them one by one): output rows within the
-floored relative error 2e-2, using the GPU's routing.
+give exact zero rows; two runs bitwise equal; the separate calls give the
+layer's output bit for bit.
+
+Outputs, stage by stage.  Each bf16 rounding point (h, y_packed, y) is a
+quantisation decided in floating point, so, as for routing, each stage is
+compared with the oracle evaluated on the GPU's own stored input to that
+stage: h on the gathered rows (exact), y_packed on the GPU's h, y on the GPU's
+y_packed and routing weights.  Each must sit within one bf16 step (floored
+relative error 1e-2), on every row of the four DeepSeek-V3-shaped workloads;
+on the dense 16384-token workload, whose float64 experts take minutes on the
+host, h and y_packed are compared on a seeded quarter of each expert's rows
+and y on every row.  The oracle run end to end from the same routing (its own
+h and y_packed) is reported beside it: a one-step difference in h can move an
+element of y_packed across a rounding boundary, which the gate weight then
+carries into y, so this chained error is a diagnostic, not the bar.
 """
 import numpy as np
 import pytest
@@ -14,23 +26,50 @@ import pytest
 import combine_router_top_amd as M
 import oracle.moe_oracle as O
 import workloads
-from tests.gpu_util import check_routing, dev, host, near_tie_tokens
-from tests.metrics import TOL
+from tests.gpu_util import check_close, check_routing, dev, host, near_tie_tokens
+from tests.metrics import STAGE_TOL, TOL, floored_rel_err
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["dsv3_decode", "dsv3_prefill", "dsv3_decode_skew", "dsv3_prefill_skew", "dense8_prefill"]
+# workloads whose expert stages are compared on a fraction of each expert's rows
+SAMPLED = {"dense8_prefill": 0.25}
 
 
-def _sample_tokens(inv2, T, n=40, seed=0):
-    nloc = (inv2 >= 0).sum(1)
+def _sample_rows(offsets, frac, seed=0):
+    """A seeded, sorted selection of about frac of every segment's rows, always
+    with the segment's first and last row; and the offsets of the selection."""
     rng = np.random.default_rng(seed)
-    pick = {0, T - 1, int(np.argmax(nloc))}
-    zero = np.nonzero(nloc == 0)[0]
-    if zero.size:
-        pick.add(int(zero[0]))
-    pick.update(int(t) for t in rng.choice(T, size=min(n, T), replace=False))
-    return sorted(pick)
+    sel, off = [], [0]
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            pick = {r0, r1 - 1}
+            pick.update(int(r) for r in rng.choice(np.arange(r0, r1), size=max(1, int(frac * (r1 - r0))),
+                                                   replace=False))
+            sel.extend(sorted(pick))
+        off.append(len(sel))
+    return np.array(sel, dtype=np.int64), np.array(off, dtype=np.int32)
+
+
+def _chained_report(w, inp, gi, gw, yg, inv2, frac):
+    """The oracle end to end from the GPU's routing, on all tokens (or, for a
+    sampled workload, a seeded subset): max floored error, elements above the
+    end-to-end bar, and the 99.999th percentile."""
+    if frac is None:
+        ref = O.moe_layer(w, inp, routing={"topk_idx": gi, "topk_w": gw})["y"]
+        got = yg
+        what = f"all {w.T} tokens"
+    else:
+        rng = np.random.default_rng(1)
+        toks = sorted(set(int(t) for t in rng.choice(w.T, size=256, replace=False)) | {0, w.T - 1})
+        ref = O.token_outputs(w, inp, gi, gw, toks)
+        got = yg[toks]
+        what = f"{len(toks)} sampled tokens"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    e = np.abs(got - ref) / np.maximum(np.abs(ref), rms)
+    return (f"chained oracle on {what}: max {e.max():.3e}, above {TOL[w.dtype]:g}: "
+            f"{int((e > TOL[w.dtype]).sum())} of {e.size}, q99.999 {np.quantile(e, 0.99999):.3e}")
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -48,8 +87,7 @@ def test_layer_full_size(name):
     torch.cuda.synchronize()
     yh = host(y)
     assert np.array_equal(yh, host(y2)), "two runs differ"
-    del d, y2
-    torch.cuda.empty_cache()
+    del y2
 
     gl, gi, gw = host(r["logits"]), host(r["topk_idx"]), host(r["topk_w"])
     ref_l = O.router_logits(inp["x"], inp["w_gate"], w.dtype, inp["bias"])
@@ -67,16 +105,36 @@ def test_layer_full_size(name):
     none = ~(inv2 >= 0).any(1)
     assert not np.any(yh[none]), "tokens with no local slot must give zero rows"
 
-    toks = _sample_tokens(inv2, w.T)
-    ref = O.token_outputs(w, inp, gi, gw, toks)
-    got = O.widen(yh[toks], w.dtype)
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    err = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
-    # diagnostic only: the same rows in exact float64, with no bf16 rounding
-    # point, show how much of the error is the stored precision itself
-    ex = O.token_outputs(w, inp, gi, gw, toks, rounded=False)
-    rms_x = float(np.sqrt(np.mean(ex * ex)))
-    err_x = float(np.max(np.abs(got - ex) / np.maximum(np.abs(ex), rms_x)))
-    print(f"[full-size] {name}: A={A} sampled {len(toks)} tokens, y err {err:.3e}"
-          f" (vs unrounded float64 {err_x:.3e})", flush=True)
-    assert err <= TOL[w.dtype], err
+    # the same layer through the separate calls exposes h and y_packed
+    idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, d["x"])
+    h, yp = M.expert_gemm(p, o["x_packed"], o["offsets"], d["w1"], d["w3"], d["w2"])
+    ys = M.combine(p, yp, o["inv"], wt)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), gi) and np.array_equal(host(wt), gw)
+    assert np.array_equal(host(ys), yh), "separate calls differ from moe_layer"
+    xp = host(o["x_packed"])[:A]
+    assert np.array_equal(xp, O.gather_rows(inp["x"], perm, w.k))
+    hg = O.widen(host(h)[:A], w.dtype)
+    ypg = O.widen(host(yp)[:A], w.dtype)
+    del d, o, h, yp, ys, idx, wt
+    torch.cuda.empty_cache()
+
+    frac = SAMPLED.get(name)
+    if frac is None:
+        rows, soff = np.arange(A), offsets
+    else:
+        rows, soff = _sample_rows(offsets, frac)
+    print(f"[full-size] {name}: oracle stages on {rows.size} of {A} packed rows", flush=True)
+    hr, _ = O.swiglu_experts(xp[rows], soff, inp["w1"], inp["w3"], inp["w2"], w.dtype)
+    eh = check_close(hg[rows], hr, w.dtype, "h (oracle on the GPU's x_packed)", STAGE_TOL[w.dtype])
+    del hr
+    ypr = O.down_projection(hg[rows], soff, inp["w2"], w.dtype)
+    ey = check_close(ypg[rows], ypr, w.dtype, "y_packed (oracle on the GPU's h)", STAGE_TOL[w.dtype])
+    del ypr
+    yr = O.combine(ypg, inv, gw, w.dtype)
+    yg = O.widen(yh, w.dtype)
+    e_y = check_close(yg, yr, w.dtype, "y (oracle on the GPU's y_packed)", STAGE_TOL[w.dtype])
+    print(f"[full-size] {name}: A={A} stage errors h {eh:.3e} y_packed {ey:.3e} y {e_y:.3e}"
+          f" (bar {STAGE_TOL[w.dtype]:g})", flush=True)
+    print(f"[full-size] {name}: " + _chained_report(w, inp, gi, gw, yg, inv2, frac), flush=True)

@@ -40,7 +40,9 @@ def test_gemm_signal(shape):
 
 def test_tile_forward_concurrent():
     """The forwarder polls on a second stream while the GEMM runs: every tile
-    it copies must already be final (dst == C bit for bit), none times out."""
+    it copies must already be final (dst == C bit for bit), none times out.
+    Both streams start after the host synchronisation, so the forwarder can
+    only overlap the GEMM, never precede its launch."""
     import torch
     Mr, N, K = 2048, 2048, 1024
     A, B = _operands(Mr, N, K, seed=3)
@@ -55,9 +57,12 @@ def test_tile_forward_concurrent():
     for epoch in (1, 2):
         dst.zero_()
         torch.cuda.synchronize()
+        # the GEMM is enqueued first: if the two streams share a hardware
+        # queue, the forwarder then runs after it (every flag already set)
+        # instead of spinning in front of it
+        M.gemm_signal(dA, dB, flags, epoch, stream=s1, out=C)
         M.tile_forward(C, dst, flags, epoch, spin_limit=1 << 22, timeouts=timeouts, workgroups=4,
                        stream=s2)
-        M.gemm_signal(dA, dB, flags, epoch, stream=s1, out=C)
         torch.cuda.synchronize()
         assert int(host(timeouts)[0]) == 0
         assert np.array_equal(host(dst), host(C))

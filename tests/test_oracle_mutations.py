@@ -106,12 +106,27 @@ def _experts_no_h_rounding(x_packed, offsets, w1, w3, w2, dtype):
     return h, y
 
 
-def _combine_unweighted(y_packed, inv, topk_w, dtype):
+def _combine_unweighted(y_packed, inv, topk_w, dtype, k=None):
+    if topk_w is None:
+        return _real["combine"](y_packed, inv, None, dtype, k=k)
     return _real["combine"](y_packed, inv, np.ones_like(topk_w), dtype)
 
 
-def _combine_wrong_slot(y_packed, inv, topk_w, dtype):
+def _combine_wrong_slot(y_packed, inv, topk_w, dtype, k=None):
+    if topk_w is None:
+        return _real["combine"](y_packed, inv, None, dtype, k=k)
     return _real["combine"](y_packed, inv, np.asarray(topk_w)[:, ::-1].copy(), dtype)
+
+
+def _down_projection_ignores_scale(h, offsets, w2, dtype, row_scale=None):
+    return _real["down_projection"](h, offsets, w2, dtype)
+
+
+def _down_projection_scale_after_rounding(h, offsets, w2, dtype, row_scale=None):
+    y = _real["down_projection"](h, offsets, w2, dtype)
+    if row_scale is None:
+        return y
+    return _real["rnd"](np.asarray(row_scale, dtype=np.float64)[:, None] * y, dtype)
 
 
 def _dispatch_padded_keeps_last(topk_idx, E, lo, n, C):
@@ -160,6 +175,8 @@ MUTATIONS = {
     "swiglu_h_not_rounded": ("swiglu_experts", _experts_no_h_rounding),
     "combine_drops_weight": ("combine", _combine_unweighted),
     "combine_wrong_slot_weight": ("combine", _combine_wrong_slot),
+    "down_projection_ignores_scale": ("down_projection", _down_projection_ignores_scale),
+    "down_projection_scale_after_rounding": ("down_projection", _down_projection_scale_after_rounding),
 }
 
 
