@@ -9,6 +9,7 @@ call raises.
 Functions (same names as the C calls):
     route(p, x, w_gate, bias=None, want_logits=False) -> (topk_idx, topk_w[, logits])
     dispatch(p, topk_idx, x) -> dict(counts_all, offsets, perm, inv, x_packed)
+    dispatch_noalloc(p, topk_idx, x) -> the same, with no workspace (static scratch)
     expert_gemm(p, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
     combine(p, y_packed, inv, topk_w) -> y
     layer(p, x, w_gate, bias, w1, w3, w2, routing=False, overlap=False, ...) -> y or (y, dict)
@@ -36,7 +37,8 @@ MOE_SCOPE_AGENT, MOE_SCOPE_SYSTEM = 0, 1
 
 EXPORTED = ["moe_last_error", "moe_version", "moe_workspace_bytes", "moe_route", "moe_dispatch",
             "moe_expert_gemm", "moe_combine", "moe_layer", "moe_dispatch_padded",
-            "moe_expert_gemm_padded", "moe_gemm_signal_tiles", "moe_gemm_signal", "moe_tile_forward"]
+            "moe_expert_gemm_padded", "moe_gemm_signal_tiles", "moe_gemm_signal", "moe_tile_forward",
+            "moe_dispatch_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -74,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_dispatch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_expert_gemm.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp]
         L.moe_layer.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(RoutingOut), vp, sz,
@@ -87,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.moe_tile_forward.argtypes = [i32, i32, vp, vp, vp, u32, u32, i32, vp, i32, vp]
         for n in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_layer",
                   "moe_dispatch_padded", "moe_expert_gemm_padded", "moe_gemm_signal",
-                  "moe_tile_forward"):
+                  "moe_tile_forward", "moe_dispatch_noalloc"):
             getattr(L, n).restype = i32
         _lib = L
     return _lib
@@ -196,10 +199,7 @@ def route(p: Spec, x, w_gate, bias=None, want_logits: bool = False, workspace=No
     return (idx, w, logits) if want_logits else (idx, w)
 
 
-def dispatch(p: Spec, topk_idx, x, workspace=None, stream=None, out=None) -> Dict[str, object]:
-    """Returns counts_all, offsets, perm, inv, x_packed.  Fresh outputs are
-    pre-filled (perm with -7, x_packed with 0) so that untouched rows are
-    visible; ``out`` (a dict of the same tensors) is written in place."""
+def _dispatch_out(p: Spec, topk_idx, x, out):
     torch = _torch()
     dt = _dt(p)
     _need(topk_idx, (p.T, p.k), torch.int32, "topk_idx")
@@ -217,12 +217,32 @@ def dispatch(p: Spec, topk_idx, x, workspace=None, stream=None, out=None) -> Dic
     _need(o["perm"], (p.rows_max,), torch.int32, "perm")
     _need(o["inv"], (p.T * p.k,), torch.int32, "inv")
     _need(o["x_packed"], (p.rows_max, p.d), dt, "x_packed")
-    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_DISPATCH, dev)
+    return o
+
+
+def dispatch(p: Spec, topk_idx, x, workspace=None, stream=None, out=None) -> Dict[str, object]:
+    """Returns counts_all, offsets, perm, inv, x_packed.  Fresh outputs are
+    pre-filled (perm with -7, x_packed with 0) so that untouched rows are
+    visible; ``out`` (a dict of the same tensors) is written in place."""
+    o = _dispatch_out(p, topk_idx, x, out)
+    ws = workspace if workspace is not None else alloc_workspace(p, MOE_CALL_DISPATCH, x.device)
     pc = p.c()
     _check(lib().moe_dispatch(ctypes.byref(pc), _ptr(topk_idx), _ptr(x), _ptr(o["counts_all"]),
                               _ptr(o["offsets"]), _ptr(o["perm"]), _ptr(o["inv"]),
                               _ptr(o["x_packed"]), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(stream)))
+    return o
+
+
+def dispatch_noalloc(p: Spec, topk_idx, x, stream=None, out=None) -> Dict[str, object]:
+    """moe_dispatch_noalloc: the same outputs as ``dispatch`` with no
+    workspace (the library's static per-device scratch; calls that overlap on
+    one device race)."""
+    o = _dispatch_out(p, topk_idx, x, out)
+    pc = p.c()
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(pc), _ptr(topk_idx), _ptr(x),
+                                      _ptr(o["counts_all"]), _ptr(o["offsets"]), _ptr(o["perm"]),
+                                      _ptr(o["inv"]), _ptr(o["x_packed"]), _stream(stream)))
     return o
 
 

@@ -21,6 +21,7 @@
 // A batch of at most 1024 assignments (one chunk, e.g. decode) launches only
 // the scatter kernel, whose single workgroup builds the histogram itself.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -314,6 +315,42 @@ __global__ __launch_bounds__(256) void gather_padded_kernel(const u32x4* __restr
 static int64_t n_chunks(const Prob& p) { return (p.tk() + DCH - 1) / DCH; }
 
 size_t dispatch_ws_bytes(const Prob& p) { return (size_t)n_chunks(p) * p.E * sizeof(int32_t); }
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free dispatch: the per-chunk histograms live in a
+// static device array instead of a caller workspace.  Each device holds its
+// own copy for the life of the process; its device address is looked up once
+// per device (with that device current) and kept.  In host code the array's
+// name is only a registration handle, so kernels get the looked-up address.
+// Every call on a device shares the array: calls that overlap on one device
+// race.  The histogram kernel writes every entry that the scatter kernel later
+// reads, so nothing has to start at zero.
+// ---------------------------------------------------------------------------
+constexpr size_t DISPATCH_SCRATCH_BYTES = size_t(1) << 20;
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static __device__ __align__(256) int32_t scratch[DISPATCH_SCRATCH_BYTES / sizeof(int32_t)];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[SCRATCH_MAX_DEVICES] = {};
+
+size_t dispatch_scratch_bytes() { return DISPATCH_SCRATCH_BYTES; }
+
+hipError_t dispatch_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
 
 // Empty batch: the histogram over all E experts and the local offsets are all
 // zero; one workgroup writes them (a kernel rather than a memset, so that the

@@ -21,6 +21,10 @@ hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* cou
 // Zero counts_all [E] and offsets [n+1] (either may be NULL): the index of an
 // empty batch.  launch_dispatch_index does this itself when T = 0.
 hipError_t launch_clear_index(const Prob& p, int32_t* counts_all, int32_t* offsets, hipStream_t st);
+// Static per-device scratch of the allocation-free dispatch: its size, and its
+// device address on the current device (looked up once per device).
+size_t dispatch_scratch_bytes();
+hipError_t dispatch_scratch(void** out);
 // Gather rows of the local experts [e_begin, e_end) (0-based local indices).
 hipError_t launch_gather(const Prob& p, const void* x, const int32_t* offsets,
                          const int32_t* perm, void* x_packed, int e_begin, int e_end,

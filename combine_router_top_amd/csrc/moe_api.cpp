@@ -254,6 +254,42 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, const
   return hip_status(e, "moe_dispatch");
 }
 
+moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const int32_t* topk_idx, const void* x,
+                                  int32_t* counts_all, int32_t* offsets, int32_t* perm,
+                                  int32_t* inv, void* x_packed, void* stream) {
+  moe::Prob q;
+  moe_status_t st = check_problem(p, &q);
+  if (st != MOE_OK) return st;
+  NEED_PTR(counts_all);
+  NEED_PTR(offsets);
+  if (q.T == 0) {  // empty batch: all counts and offsets are zero, no scratch used
+    (void)hipGetLastError();
+    return hip_status(moe::launch_clear_index(q, counts_all, offsets, (hipStream_t)stream),
+                      "moe_dispatch_noalloc");
+  }
+  NEED_PTR(topk_idx);
+  NEED_PTR(x);
+  NEED_PTR(perm);
+  NEED_PTR(inv);
+  NEED_PTR(x_packed);
+  NEED_ALIGNED(x);
+  NEED_ALIGNED(x_packed);
+  const size_t need = moe::dispatch_ws_bytes(q);
+  if (need > moe::dispatch_scratch_bytes())
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_dispatch_noalloc: needs %zu bytes of scratch (ceil(T*k/1024)*E*4), the static "
+                "array holds %zu",
+                need, moe::dispatch_scratch_bytes());
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  void* scr = nullptr;
+  hipError_t e = moe::dispatch_scratch(&scr);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch_index(q, topk_idx, counts_all, offsets, perm, inv, scr, s);
+  if (e == hipSuccess) e = moe::launch_gather(q, x, offsets, perm, x_packed, 0, q.n, s);
+  return hip_status(e, "moe_dispatch_noalloc");
+}
+
 moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, void* h,
                              void* y_packed, void* workspace, size_t workspace_bytes,

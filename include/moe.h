@@ -174,6 +174,23 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const int32_t* topk_idx, const
                           void* x_packed, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_dispatch without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, outputs and contract as moe_dispatch
+ * minus the workspace: its per-chunk histograms live in a static device array
+ * of MOE_DISPATCH_NOALLOC_SCRATCH_BYTES that each device holds until the
+ * process ends.  A problem needing more, ceil(T*k/1024) * E * 4 bytes (T*k up
+ * to 2^20 at E = 256), is rejected with MOE_ERR_UNSUPPORTED before anything
+ * is launched.  Every call on a device shares that array: calls that overlap
+ * on one device (several streams or host threads) race, and the caller must
+ * order them.  The call allocates nothing.
+ */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (1u << 20)
+moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const int32_t* topk_idx, const void* x,
+                                  int32_t* counts_all, int32_t* offsets, int32_t* perm,
+                                  int32_t* inv, void* x_packed, void* stream);
+
+/*
  * Local expert compute (CUCo, Abstract: "local compute" of the MoE layer).
  * For each local expert e and its rows R = [offsets[e], offsets[e+1]):
  *   h[R]        = rnd(SiLU(x_packed[R] w1[e]) * (x_packed[R] w3[e]))

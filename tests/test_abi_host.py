@@ -225,3 +225,19 @@ print(st, L.moe_last_error().decode())
     assert r.returncode == 0, r.stderr
     st, msg = r.stdout.split(" ", 1)
     assert int(st) == M.MOE_ERR_HIP and "moe_route" in msg
+
+
+def test_dispatch_noalloc_rejects_oversize():
+    """The allocation-free dispatch holds ceil(T*k/1024) * E int32 histograms in
+    a 1 MiB static array: larger problems are rejected on the host, before any
+    HIP call; so are missing pointers."""
+    L = M.lib()
+    big = M.Problem(1 << 17, 64, 1024, 8, 64, 0, 64, M.MOE_DTYPE_BF16, 0)  # 1024 chunks x 1024 experts
+    assert L.moe_dispatch_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == M.MOE_ERR_UNSUPPORTED
+    assert b"scratch" in L.moe_last_error()
+    fits = M.Problem(1 << 17, 64, 256, 8, 64, 0, 64, M.MOE_DTYPE_BF16, 0)  # 1024 chunks x 256 experts
+    assert L.moe_dispatch_noalloc(ctypes.byref(fits), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE,
+                                  None) == M.MOE_ERR_INVALID_ARG       # perm is NULL
+    assert b"perm is NULL" in L.moe_last_error()
+
