@@ -370,7 +370,7 @@ hipError_t launch_clear_index(const Prob& p, int32_t* counts_all, int32_t* offse
 
 hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                                 hipStream_t st) {
+                                 hipStream_t st, bool hist_ready) {
   if (p.tk() == 0) return launch_clear_index(p, counts_all, offsets, st);
   int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws);
   const int64_t nc = n_chunks(p);
@@ -379,10 +379,12 @@ hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* cou
                        p.n, 1, (const int32_t*)nullptr, counts_all, offsets, perm, inv);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
-                     chunk_hist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!hist_ready) {
+    hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
+                       chunk_hist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
                      p.lo, p.n, (int)nc, chunk_hist, counts_all, offsets, perm, inv);
   return hipGetLastError();

@@ -10,14 +10,22 @@ namespace moe {
 
 // route.hip
 size_t route_ws_bytes(const Prob& p);
+// chunk_hist (or NULL): the dispatch chunk histograms (hist_elems int32 =
+// ceil(T k / 1024) * E).  Where the router kernel supports it, it clears them
+// and top-k counts its selections into them; *hist_done (if given) says
+// whether that happened, so that dispatch can skip its histogram kernel.
 hipError_t launch_route(const Prob& p, const void* x, const void* wg, const float* bias,
-                        float* logits, int32_t* idx, float* w, void* ws, hipStream_t st);
+                        float* logits, int32_t* idx, float* w, void* ws, hipStream_t st,
+                        int32_t* chunk_hist = nullptr, int64_t hist_elems = 0,
+                        bool* hist_done = nullptr);
 
 // dispatch.hip
 size_t dispatch_ws_bytes(const Prob& p);
+// hist_ready: ws already holds the chunk histograms (filled by top-k), so the
+// histogram kernel is skipped.
 hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                                 hipStream_t st);
+                                 hipStream_t st, bool hist_ready = false);
 // Zero counts_all [E] and offsets [n+1] (either may be NULL): the index of an
 // empty batch.  launch_dispatch_index does this itself when T = 0.
 hipError_t launch_clear_index(const Prob& p, int32_t* counts_all, int32_t* offsets, hipStream_t st);

@@ -493,9 +493,15 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   const bool overlap = (q.flags & MOE_F_OVERLAP) && s1 != nullptr && q.n >= 2;
 
   (void)hipGetLastError();
-  hipError_t e = moe::launch_route(q, x, w_gate, bias, logits, idx, w, ws + L.route, s0);
+  // top-k fills the dispatch chunk histograms where the router supports it,
+  // which saves dispatch its histogram kernel
+  bool hist_done = false;
+  int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws + L.disp);
+  const int64_t hist_elems = (int64_t)(moe::dispatch_ws_bytes(q) / sizeof(int32_t));
+  hipError_t e = moe::launch_route(q, x, w_gate, bias, logits, idx, w, ws + L.route, s0, chunk_hist,
+                                   hist_elems, &hist_done);
   if (e == hipSuccess)
-    e = moe::launch_dispatch_index(q, idx, counts, offsets, perm, inv, ws + L.disp, s0);
+    e = moe::launch_dispatch_index(q, idx, counts, offsets, perm, inv, ws + L.disp, s0, hist_done);
   if (e != hipSuccess) return hip_status(e, "moe_layer routing");
   // bf16 with x inside one 32-bit buffer descriptor: GEMM-1 gathers the x rows
   // itself through perm, so x_packed is never written

@@ -73,6 +73,12 @@ SMALL = {
     # that fills the last round: 32 x 16 and 16 x 16 blocks)
     "thin_tcols448": W("thin_tcols448", 64, 7168, 32, 2, 64, 0, 32, "bf16", seed=26),
     "thin_tcols384": W("thin_tcols384", 48, 6144, 16, 2, 64, 0, 16, "bf16", seed=27),
+    # router on direct-to-LDS copies (>= 8 token blocks of 128, E % 8 == 0,
+    # E >= 128): ragged last token block (76 rows), 3 K splits with a K tail
+    # (1000 = 15 x 64 + 40), skew bias; and two 256-expert column blocks, the
+    # second with 64 valid experts
+    "router_dma_tails": W("router_dma_tails", 1100, 1000, 256, 8, 64, 0, 32, "bf16", skew=True, seed=34),
+    "router_dma_e320": W("router_dma_e320", 1030, 512, 320, 6, 48, 100, 40, "bf16", seed=35),
     # medium GEMM-1 blocks of the full 512 weight columns at a small size
     # (64 experts x 1024 h columns, ~50 rows each: 256 blocks fill one round)
     "medium_w512": W("medium_w512", 1600, 64, 64, 2, 1024, 0, 64, "bf16", seed=28),
@@ -102,7 +108,7 @@ def test_route(name):
 @pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
                                   "wide_ksplit", "wide_e20", "topk_e96",
                                   "topk_e384", "topk_e1024", "router_long", "topk_deep_e256",
-                                  "topk_deep_e1024"])
+                                  "topk_deep_e1024", "router_dma_tails", "router_dma_e320"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
