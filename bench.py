@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_prefill")
     ap.add_argument("--overlap", action="store_true", help="two-stream dispatch overlap")
+    ap.add_argument("--fold", action="store_true",
+                    help="routing weights applied in the down projection (MOE_F_FOLD_WEIGHT)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-gib", type=float, default=1.0,
@@ -525,9 +527,9 @@ def main():
     y = torch.empty((w.T, w.d), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
                     device="cuda")
 
-    def step():
+    def step(fold=a.fold):
         M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], overlap=a.overlap,
-                workspace=ws, stream=stream, stream2=s2, out=y)
+                workspace=ws, stream=stream, stream2=s2, out=y, fold_weight=fold)
 
     # routing statistics (outside any timed region)
     _, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True)
@@ -559,6 +561,20 @@ def main():
     per_step = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(a.steps)])
     step_stats = {"p10_ms": float(np.percentile(per_step, 10)), "median_ms": float(np.median(per_step)),
                   "p90_ms": float(np.percentile(per_step, 90)), "steps": a.steps}
+    # A/B: the same steps with the routing weights applied in combine (plain)
+    # and in the down projection's epilogue (fold), alternating blocks of steps
+    fold_ab = {"plain_ms": [], "fold_ms": []}
+    for rep in range(3):
+        for fold in (False, True):
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            step(fold)
+            f0.record(stream)
+            for _ in range(a.steps):
+                step(fold)
+            f1.record(stream)
+            torch.cuda.synchronize()
+            fold_ab["fold_ms" if fold else "plain_ms"].append(f0.elapsed_time(f1) / a.steps)
+    fold_ab = {k: float(np.median(v)) for k, v in fold_ab.items()}
 
     # each ABI call on its own, HIP events on the launch stream between calls
     idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
@@ -587,9 +603,11 @@ def main():
         if it >= 2:
             for j, n in enumerate(names):
                 tot[n] += ev[j].elapsed_time(ev[j + 1])
-    # the same calls cold: before each, a 1 GiB fill evicts the L2s and the
-    # 256 MB MALL, so every operand comes from HBM
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # the same calls cold: before each, a read pass over 1 GiB evicts the L2s
+    # and the 256 MB MALL, so every operand comes from HBM.  The pass only
+    # reads, so the caches it leaves hold clean lines: a fill instead would
+    # leave 256 MB of dirty lines whose write-back the next call would pay for.
+    flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
     cold = {n: 0.0 for n in names}
     calls = [
         lambda: M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt)),
@@ -600,7 +618,7 @@ def main():
     cold_iters = 5
     for it in range(cold_iters + 1):
         for j, n in enumerate(names):
-            flush.fill_((it + j) & 0xFF)
+            flush.sum()
             ev[0].record(stream)
             calls[j]()
             ev[1].record(stream)
@@ -649,11 +667,12 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
                    "local_experts": [w.expert_lo, w.expert_lo + w.n_local - 1],
                    "skew_bias": w.skew, "A_local": A, "active_local_experts": active,
-                   "overlap": a.overlap},
+                   "overlap": a.overlap, "fold_weight": a.fold},
         "roofline": roof,
         "phases": phases,
         "phases_cold": phases_cold,
         "step_stats": step_stats,
+        "fold_weight_ab": fold_ab,
         "wall_ms_per_step": wall / a.steps * 1e3,
         "hbm_copy": copy,
         "hbm_read": rd,

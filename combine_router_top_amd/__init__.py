@@ -12,7 +12,9 @@ Functions (same names as the C calls):
     dispatch_noalloc(p, topk_idx, x) -> the same, with no workspace (static scratch)
     expert_gemm(p, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
     combine(p, y_packed, inv, topk_w) -> y
-    layer(p, x, w_gate, bias, w1, w3, w2, routing=False, overlap=False, ...) -> y or (y, dict)
+    layer(p, x, w_gate, bias, w1, w3, w2, routing=False, overlap=False, fold_weight=False, ...)
+        -> y or (y, dict)
+    layer_ws_offset(p, MOE_WS_H | MOE_WS_Y_PACKED) -> byte offset in the layer workspace
     dispatch_padded(p, capacity, topk_idx, x) -> dict(counts_all, offsets, perm, inv, x_packed)
     expert_gemm_padded(p, capacity, x_packed, offsets, w1, w3, w2) -> (h, y_packed)
     gemm_signal(A, B, flags, epoch) -> C          (C = rnd(A B), a flag per 256 x 256 tile)
@@ -30,7 +32,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
-MOE_F_WRITE_LOGITS, MOE_F_OVERLAP = 1, 2
+MOE_F_WRITE_LOGITS, MOE_F_OVERLAP, MOE_F_FOLD_WEIGHT = 1, 2, 4
+MOE_WS_H, MOE_WS_Y_PACKED = 0, 1
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_EXPERT_GEMM, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
 MOE_CALL_DISPATCH_PADDED, MOE_CALL_EXPERT_GEMM_PADDED = 5, 6
 MOE_SCOPE_AGENT, MOE_SCOPE_SYSTEM = 0, 1
@@ -38,7 +41,7 @@ MOE_SCOPE_AGENT, MOE_SCOPE_SYSTEM = 0, 1
 EXPORTED = ["moe_last_error", "moe_version", "moe_workspace_bytes", "moe_route", "moe_dispatch",
             "moe_expert_gemm", "moe_combine", "moe_layer", "moe_dispatch_padded",
             "moe_expert_gemm_padded", "moe_gemm_signal_tiles", "moe_gemm_signal", "moe_tile_forward",
-            "moe_dispatch_noalloc"]
+            "moe_dispatch_noalloc", "moe_layer_ws_offset"]
 
 
 class MoeError(RuntimeError):
@@ -74,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.moe_version.restype = ctypes.c_char_p
         L.moe_workspace_bytes.argtypes = [P, i32]
         L.moe_workspace_bytes.restype = sz
+        L.moe_layer_ws_offset.argtypes = [P, i32]
+        L.moe_layer_ws_offset.restype = sz
         L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -270,12 +275,13 @@ def expert_gemm(p: Spec, x_packed, offsets, w1, w3, w2, workspace=None, stream=N
 
 def combine(p: Spec, y_packed, inv, topk_w, stream=None, out=None, rows: Optional[int] = None):
     """``rows``: rows of y_packed (default rows_max; n_local * capacity for
-    the padded layout)."""
+    the padded layout).  ``topk_w=None`` sums the rows unweighted."""
     torch = _torch()
     dt = _dt(p)
     _need(y_packed, (p.rows_max if rows is None else rows, p.d), dt, "y_packed")
     _need(inv, (p.T * p.k,), torch.int32, "inv")
-    _need(topk_w, (p.T, p.k), torch.float32, "topk_w")
+    if topk_w is not None:
+        _need(topk_w, (p.T, p.k), torch.float32, "topk_w")
     y = torch.empty((p.T, p.d), dtype=dt, device=y_packed.device) if out is None else out
     pc = p.c()
     _check(lib().moe_combine(ctypes.byref(pc), _ptr(y_packed), _ptr(inv), _ptr(topk_w), _ptr(y),
@@ -380,11 +386,24 @@ def tile_forward(C, dst, flags, epoch: int, spin_limit: int, timeouts, workgroup
     return dst
 
 
+def layer_ws_offset(p: Spec, what: int) -> int:
+    """Byte offset of h (MOE_WS_H) or y_packed (MOE_WS_Y_PACKED) inside a
+    moe_layer workspace of problem p."""
+    pc = p.c()
+    n = int(lib().moe_layer_ws_offset(ctypes.byref(pc), int(what)))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoeError(MOE_ERR_INVALID_ARG, lib().moe_last_error().decode())
+    return n
+
+
 def layer(p: Spec, x, w_gate, bias, w1, w3, w2, routing: bool = False, want_logits: bool = False,
-          overlap: bool = False, workspace=None, stream=None, stream2=None, out=None):
+          overlap: bool = False, workspace=None, stream=None, stream2=None, out=None,
+          fold_weight: bool = False):
     """The whole layer.  With ``routing`` also returns the routing/dispatch
     tensors; with ``overlap`` runs the two-stream dispatch overlap (needs
-    ``stream2``, a torch.cuda.Stream, or creates none and runs one stream)."""
+    ``stream2``, a torch.cuda.Stream, or creates none and runs one stream);
+    with ``fold_weight`` the routing weights scale the expert output rows in
+    the down projection and combine sums them unweighted."""
     torch = _torch()
     dt = _dt(p)
     _need(x, (p.T, p.d), dt, "x")
@@ -395,7 +414,8 @@ def layer(p: Spec, x, w_gate, bias, w1, w3, w2, routing: bool = False, want_logi
     _need(w3, (p.n_local, p.d, p.f), dt, "w3")
     _need(w2, (p.n_local, p.f, p.d), dt, "w2")
     dev = x.device
-    flags = p.flags | (MOE_F_WRITE_LOGITS if want_logits else 0) | (MOE_F_OVERLAP if overlap else 0)
+    flags = (p.flags | (MOE_F_WRITE_LOGITS if want_logits else 0) | (MOE_F_OVERLAP if overlap else 0)
+             | (MOE_F_FOLD_WEIGHT if fold_weight else 0))
     q = Spec(p.T, p.d, p.E, p.k, p.f, p.expert_lo, p.n_local, p.dtype, flags)
     y = torch.empty((p.T, p.d), dtype=dt, device=dev) if out is None else out
     r = None

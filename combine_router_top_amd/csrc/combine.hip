@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
   float my_w = 0.f;
   if (lane < k) {
     my_row = inv[t * k + lane];
-    my_w = w[t * k + lane];
+    my_w = w ? w[t * k + lane] : 1.0f;   // no weights: rows already weighted, a plain sum
   }
   // compact the local slots into LDS, keeping slot order
   const uint64_t valid = __ballot(my_row >= 0);

@@ -79,7 +79,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
                                                       int32_t* __restrict__ counts_all,
                                                       int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ inv) {
+                                                      int32_t* __restrict__ inv,
+                                                      const float* __restrict__ w_in,
+                                                      float* __restrict__ rscale) {
   __shared__ int base[DMAXE];
   __shared__ int wpos[4][DMAXE];
   __shared__ int scan_tmp[4];
@@ -219,7 +221,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     __builtin_amdgcn_wave_barrier();
     if (a < TK) {
       inv[a] = pos;
-      if (valid) perm[pos] = (int32_t)a;
+      if (valid) {
+        perm[pos] = (int32_t)a;
+        if (rscale) rscale[pos] = w_in[a];
+      }
     }
   }
 }
@@ -370,13 +375,13 @@ hipError_t launch_clear_index(const Prob& p, int32_t* counts_all, int32_t* offse
 
 hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                                 hipStream_t st, bool hist_ready) {
+                                 hipStream_t st, bool hist_ready, const float* w_in, float* rscale) {
   if (p.tk() == 0) return launch_clear_index(p, counts_all, offsets, st);
   int32_t* chunk_hist = reinterpret_cast<int32_t*>(ws);
   const int64_t nc = n_chunks(p);
   if (nc == 1) {  // one workgroup does it all
     hipLaunchKernelGGL(scatter_kernel<true>, dim3(1), dim3(256), 0, st, idx, p.tk(), p.E, p.lo,
-                       p.n, 1, (const int32_t*)nullptr, counts_all, offsets, perm, inv);
+                       p.n, 1, (const int32_t*)nullptr, counts_all, offsets, perm, inv, w_in, rscale);
     return hipGetLastError();
   }
   if (!hist_ready) {
@@ -386,7 +391,7 @@ hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* cou
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(scatter_kernel<false>, dim3((unsigned)nc), dim3(256), 0, st, idx, p.tk(), p.E,
-                     p.lo, p.n, (int)nc, chunk_hist, counts_all, offsets, perm, inv);
+                     p.lo, p.n, (int)nc, chunk_hist, counts_all, offsets, perm, inv, w_in, rscale);
   return hipGetLastError();
 }
 

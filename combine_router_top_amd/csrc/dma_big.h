@@ -317,13 +317,14 @@ __device__ __forceinline__ void bd_accum(const bf16_t* __restrict__ A, int64_t l
 // the abytes-byte matrix A; weight column block nt of expert e.  K and N
 // multiples of 8.
 //   SWIGLU: C[r0 + r][128 nt + h] = rnd(SiLU(A W1) * (A W3)), B1/B3 = [E][K][N]
-//   else:   C[r0 + r][256 nt + n] = rnd(A W2),                 B1 = [E][K][N]
+//   else:   C[r0 + r][256 nt + n] = rnd(s (A W2)),             B1 = [E][K][N]
+// with s = rscale[r0 + r], or 1 when rscale is NULL.
 template <bool SWIGLU, int NW>
 __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                         const bf16_t* __restrict__ B3, int K, int N,
                                         bf16_t* __restrict__ C, int e, int r0, int R, int nt,
                                         const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
-                                        char* ring) {
+                                        const float* __restrict__ rscale, char* ring) {
   constexpr int MT = BdCfg<NW>::MT;
   const int64_t estride = (int64_t)K * N;
   f32x4 acc[MT][8];
@@ -336,6 +337,7 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int row = 16 * MT * wm + 16 * mt + i;
+    const float sc = !SWIGLU && rscale && row < R ? rscale[r0 + row] : 1.0f;
 #pragma unroll
     for (int t = 0; t < (SWIGLU ? 4 : 8); ++t) {
       const int col = SWIGLU ? 128 * nt + 64 * wn + 16 * t + 4 * g : 256 * nt + 128 * wn + 16 * t + 4 * g;
@@ -343,7 +345,7 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acc[mt][t][r];
-        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a;
+        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a * sc;
       }
       if (row < R && col < N)
         *reinterpret_cast<u32x2*>(C + (int64_t)(r0 + row) * N + col) =

@@ -198,13 +198,14 @@ __device__ __forceinline__ void dt_trip(const DtCtx<MT>& c, const DtSlots& S, in
 // GEMM-2: output columns mcols * nb .. + mcols - 1).  A row r is A[r0 + r] or, with a row map, row
 // rows[r0 + r] / rdiv of the abytes-byte matrix A.  K and N multiples of 8.
 //   SWIGLU: C[r0 + r][h] = rnd(SiLU(A W1) * (A W3)),  B1/B3 = [E][K][N]
-//   else:   C[r0 + r][n] = rnd(A W2),                   B1 = [E][K][N]
+//   else:   C[r0 + r][n] = rnd(s (A W2)),               B1 = [E][K][N]
+// with s = rscale[r0 + r], or 1 when rscale is NULL.
 template <bool SWIGLU, int MT>
 __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B1,
                                          const bf16_t* __restrict__ B3, int K, int N,
                                          bf16_t* __restrict__ C, int e, int r0, int R, int nb, int mcols,
                                          const int32_t* __restrict__ rows, int rdiv, uint32_t abytes,
-                                         int wave, const DtSlots& S) {
+                                         const float* __restrict__ rscale, int wave, const DtSlots& S) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   const int64_t estride = (int64_t)K * N;
@@ -271,6 +272,7 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int row = 16 * MT * wm + 16 * mt + i;
+    const float sc = !SWIGLU && rscale && row < R ? rscale[r0 + row] : 1.0f;
 #pragma unroll
     for (int t = 0; t < (SWIGLU ? 4 : 8); ++t) {
       const int col = cblk + (SWIGLU ? 64 * wn : 128 * wn) + 16 * t + 4 * g;
@@ -278,7 +280,7 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acc[mt][t][r];
-        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a;
+        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a * sc;
       }
       if (row < R && col < cend)
         *reinterpret_cast<u32x2*>(C + (int64_t)(r0 + row) * N + col) =

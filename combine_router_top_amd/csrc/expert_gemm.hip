@@ -82,6 +82,10 @@ struct RowMap {
   const int32_t* rows;
   int div;
   uint32_t bytes;
+  // Optional scale of every output row (down projection only): packed row p
+  // is multiplied by scale[p] before its rounding (the routing weight of its
+  // assignment, so that combine only sums).  nullptr: no scale.
+  const float* scale = nullptr;
 };
 
 // Segments of at most XG_THIN_MAX rows stream through the thin tiles, larger
@@ -238,6 +242,11 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * mt + 4 * g + r;
       if (row < rb.R) {
+        if (!SWIGLU && rm.scale) {
+          const float sc = rm.scale[rb.r0 + row];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[mt][c][r] *= sc;
+        }
         bf16_t* dst = C + (int64_t)(rb.r0 + row) * N + col;
         if constexpr (CPL == 2) {
           *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[mt][0][r], acc[mt][1][r]);
@@ -406,7 +415,7 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
 #define XM_CASE(n)                                                                              \
   case n:                                                                                       \
     dt_block<SWIGLU, n>(A, B1, B3, K, N, C, rb.e, rb.r0, rb.R, rb.nb, mcols, rm.rows, rm.div,    \
-                        rm.bytes, wave, slots);                                                 \
+                        rm.bytes, rm.scale, wave, slots);                                       \
     break;
     XM_CASE(1) XM_CASE(2) XM_CASE(3) XM_CASE(4) XM_CASE(5)
 #undef XM_CASE
@@ -464,7 +473,8 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void grouped_gemm_bf16_big(
     bt.R = __builtin_amdgcn_readfirstlane(bt.R);
     bt.nt = __builtin_amdgcn_readfirstlane(bt.nt);
     __syncthreads();   // every wave has read the table before the copies overwrite it
-    bd_tile<SWIGLU, XB_NW>(A, B1, B3, K, N, C, bt.e, bt.r0, bt.R, bt.nt, rm.rows, rm.div, rm.bytes, ring);
+    bd_tile<SWIGLU, XB_NW>(A, B1, B3, K, N, C, bt.e, bt.r0, bt.R, bt.nt, rm.rows, rm.div, rm.bytes,
+                           rm.scale, ring);
   }
 }
 
@@ -503,7 +513,7 @@ __global__ __launch_bounds__(64 * XB_NW, 1) void gemm_signal_kernel(
   bt.r0 = tm * XB_BM;
   bt.R = min(XB_BM, M - bt.r0);
   bt.nt = tn;
-  bd_tile<false, XB_NW>(A, B, nullptr, K, N, C, 0, bt.r0, bt.R, bt.nt, nullptr, 1, 0, ring);
+  bd_tile<false, XB_NW>(A, B, nullptr, K, N, C, 0, bt.r0, bt.R, bt.nt, nullptr, 1, 0, nullptr, ring);
   // every thread's stores of the tile complete and visible at the scope,
   // then one release store of the flag
   if (system_scope) __threadfence_system();
@@ -538,7 +548,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
                                                         int e_begin, int e_end,
                                                         const float* __restrict__ B1,
                                                         const float* __restrict__ B3, int K, int N,
-                                                        float* __restrict__ C) {
+                                                        float* __restrict__ C,
+                                                        const float* __restrict__ rscale) {
   const int64_t p = (int64_t)offsets[e_begin] + blockIdx.x;
   if (p >= offsets[e_end]) return;
   const int n = blockIdx.y * 256 + threadIdx.x;
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
     s1 = fmaf(a[kk], B1[es + (int64_t)kk * N + n], s1);
     if (SWIGLU) s3 = fmaf(a[kk], B3[es + (int64_t)kk * N + n], s3);
   }
-  C[p * N + n] = SWIGLU ? s1 / (1.0f + expf(-s1)) * s3 : s1;
+  C[p * N + n] = SWIGLU ? s1 / (1.0f + expf(-s1)) * s3 : (rscale ? s1 * rscale[p] : s1);
 }
 
 // Compute units of the current device.
@@ -577,12 +588,12 @@ size_t expert_gemm_ws_bytes(const Prob&) { return 0; }
 hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
                               const void* w1, const void* w3, const void* w2, void* h,
                               void* y_packed, void*, int e_begin, int e_end, hipStream_t st,
-                              const int32_t* perm) {
+                              const int32_t* perm, const float* rscale) {
   if (p.rows_max == 0 || e_end <= e_begin) return hipSuccess;
   if (p.dtype == 1) {
     // with perm, x_packed is x itself and GEMM-1 reads row perm[p] / k for packed row p
     const RowMap rm1 = perm ? RowMap{perm, p.k, (uint32_t)((int64_t)p.T * p.d * 2)} : RowMap{nullptr, 1, 0};
-    const RowMap rm2{nullptr, 1, 0};
+    const RowMap rm2{nullptr, 1, 0, rscale};
     // Dense-like routing (the mean segment reaches XB_TH rows, or every
     // segment does in the padded layout): experts with >= XB_TH rows go to the
     // 256 x 256 kernel.  Otherwise every segment, however long, streams
@@ -681,13 +692,14 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);
   hipLaunchKernelGGL(grouped_gemm_f32<true>, g1, dim3(256), 0, st, (const float*)x_packed, offsets,
-                     e_begin, e_end, (const float*)w1, (const float*)w3, p.d, p.f, (float*)h);
+                     e_begin, e_end, (const float*)w1, (const float*)w3, p.d, p.f, (float*)h,
+                     (const float*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)p.rows_max, (p.d + 255) / 256);
   hipLaunchKernelGGL(grouped_gemm_f32<false>, g2, dim3(256), 0, st, (const float*)h, offsets,
                      e_begin, e_end, (const float*)w2, (const float*)nullptr, p.f, p.d,
-                     (float*)y_packed);
+                     (float*)y_packed, rscale);
   return hipGetLastError();
 }
 

@@ -23,9 +23,12 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
 size_t dispatch_ws_bytes(const Prob& p);
 // hist_ready: ws already holds the chunk histograms (filled by top-k), so the
 // histogram kernel is skipped.
+// w_in / rscale (both or neither): rscale[inv[a]] = w_in[a] for every local
+// assignment a (the routing weight of each packed row).
 hipError_t launch_dispatch_index(const Prob& p, const int32_t* idx, int32_t* counts_all,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
-                                 hipStream_t st, bool hist_ready = false);
+                                 hipStream_t st, bool hist_ready = false,
+                                 const float* w_in = nullptr, float* rscale = nullptr);
 // Zero counts_all [E] and offsets [n+1] (either may be NULL): the index of an
 // empty batch.  launch_dispatch_index does this itself when T = 0.
 hipError_t launch_clear_index(const Prob& p, int32_t* counts_all, int32_t* offsets, hipStream_t st);
@@ -50,10 +53,11 @@ hipError_t launch_dispatch_padded(const Prob& p, int capacity, const int32_t* id
 // With perm (bf16 only, T * d * 2 < 2^32), x_packed is x itself and GEMM-1
 // gathers its rows through perm (packed row p = token perm[p] / k).
 size_t expert_gemm_ws_bytes(const Prob& p);
+// With rscale (packed-row weights), y_packed row p is rnd(rscale[p] * (h W2)).
 hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
                               const void* w1, const void* w3, const void* w2, void* h,
                               void* y_packed, void* ws, int e_begin, int e_end, hipStream_t st,
-                              const int32_t* perm = nullptr);
+                              const int32_t* perm = nullptr, const float* rscale = nullptr);
 
 // expert_gemm.hip: GEMM C = rnd(A B) with a release flag per 256 x 256 tile
 int64_t gemm_signal_tiles(int M, int N);

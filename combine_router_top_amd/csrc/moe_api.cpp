@@ -43,7 +43,7 @@ moe_status_t check_problem(const moe_problem_t* p, moe::Prob* out) {
   if (p->n_local <= 0 || p->expert_lo < 0 || (int64_t)p->expert_lo + p->n_local > p->E)
     return fail(MOE_ERR_INVALID_ARG, "local experts [%d, %d+%d) not inside [0, %d)", p->expert_lo,
                 p->expert_lo, p->n_local, p->E);
-  if (p->flags & ~(uint32_t)(MOE_F_WRITE_LOGITS | MOE_F_OVERLAP))
+  if (p->flags & ~(uint32_t)(MOE_F_WRITE_LOGITS | MOE_F_OVERLAP | MOE_F_FOLD_WEIGHT))
     return fail(MOE_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
   if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
@@ -83,7 +83,7 @@ moe_status_t check_problem(const moe_problem_t* p, moe::Prob* out) {
 
 // Workspace layout of moe_layer (each region 256-byte aligned).
 struct LayerWs {
-  size_t route, idx, w, counts, offsets, perm, inv, disp, xp, h, yp, gemm, total;
+  size_t route, idx, w, counts, offsets, perm, inv, disp, xp, h, yp, gemm, rs, total;
 };
 
 LayerWs layer_ws(const moe::Prob& p) {
@@ -107,6 +107,7 @@ LayerWs layer_ws(const moe::Prob& p) {
   L.h = take((size_t)p.rows_max * p.f * es);
   L.yp = take((size_t)p.rows_max * p.d * es);
   L.gemm = take(moe::expert_gemm_ws_bytes(p));
+  L.rs = take((size_t)p.rows_max * 4);
   L.total = o;
   return L;
 }
@@ -193,7 +194,24 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
 
-const char* moe_version(void) { return "libmoe 0.1 gfx950"; }
+const char* moe_version(void) { return "libmoe 0.2 gfx950"; }
+
+size_t moe_layer_ws_offset(const moe_problem_t* p, int32_t what) {
+  moe::Prob q;
+  if (check_problem(p, &q) != MOE_OK) return (size_t)-1;
+  if (q.T == 0) {
+    fail(MOE_ERR_INVALID_ARG, "an empty batch has no layer workspace");
+    return (size_t)-1;
+  }
+  const LayerWs L = layer_ws(q);
+  switch (what) {
+    case MOE_WS_H: g_err.clear(); return L.h;
+    case MOE_WS_Y_PACKED: g_err.clear(); return L.yp;
+    default:
+      fail(MOE_ERR_INVALID_ARG, "unknown workspace region %d", what);
+      return (size_t)-1;
+  }
+}
 
 size_t moe_workspace_bytes(const moe_problem_t* p, int32_t call) {
   moe::Prob q;
@@ -431,8 +449,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int
   if (q.T == 0) return ok();  // empty batch: no output rows
   NEED_PTR(y_packed);
   NEED_PTR(inv);
-  NEED_PTR(topk_w);
-  NEED_PTR(y);
+  NEED_PTR(y);            // topk_w may be NULL: the rows are summed unweighted
   NEED_ALIGNED(y_packed);
   NEED_ALIGNED(y);
   (void)hipGetLastError();
@@ -478,6 +495,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   };
   const moe_routing_out_t none{};
   const moe_routing_out_t& ro = routing_out ? *routing_out : none;
+  const bool fold = (q.flags & MOE_F_FOLD_WEIGHT) != 0;
   int32_t* idx = pick(ro.topk_idx, L.idx);
   float* w = pick(ro.topk_w, L.w);
   int32_t* counts = pick(ro.counts_all, L.counts);
@@ -500,18 +518,24 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   const int64_t hist_elems = (int64_t)(moe::dispatch_ws_bytes(q) / sizeof(int32_t));
   hipError_t e = moe::launch_route(q, x, w_gate, bias, logits, idx, w, ws + L.route, s0, chunk_hist,
                                    hist_elems, &hist_done);
+  // with the weight folded into the down projection, the scatter also writes
+  // each packed row's routing weight
+  float* rscale = fold ? reinterpret_cast<float*>(ws + L.rs) : nullptr;
   if (e == hipSuccess)
-    e = moe::launch_dispatch_index(q, idx, counts, offsets, perm, inv, ws + L.disp, s0, hist_done);
+    e = moe::launch_dispatch_index(q, idx, counts, offsets, perm, inv, ws + L.disp, s0, hist_done,
+                                   fold ? w : nullptr, rscale);
   if (e != hipSuccess) return hip_status(e, "moe_layer routing");
   // bf16 with x inside one 32-bit buffer descriptor: GEMM-1 gathers the x rows
   // itself through perm, so x_packed is never written
   const bool fused = q.dtype == 1 && (int64_t)q.T * q.d * 2 < (int64_t(1) << 31);
   if (!overlap && fused) {
-    e = moe::launch_expert_gemm(q, x, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0, perm);
+    e = moe::launch_expert_gemm(q, x, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0, perm,
+                                rscale);
   } else if (!overlap) {
     e = moe::launch_gather(q, x, offsets, perm, xp, 0, q.n, s0);
     if (e == hipSuccess)
-      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0);
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0,
+                                  nullptr, rscale);
   } else {
     // two-stream dispatch overlap: the upper half of the local experts is
     // packed on s1 while the lower half's GEMMs run on s0.
@@ -523,12 +547,14 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
     if (e == hipSuccess) e = hipEventRecord(g_ev.b, s1);
     if (e == hipSuccess) e = moe::launch_gather(q, x, offsets, perm, xp, 0, half, s0);
     if (e == hipSuccess)
-      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, half, s0);
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, half, s0,
+                                  nullptr, rscale);
     if (e == hipSuccess) e = hipStreamWaitEvent(s0, g_ev.b, 0);
     if (e == hipSuccess)
-      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, half, q.n, s0);
+      e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, half, q.n, s0,
+                                  nullptr, rscale);
   }
-  if (e == hipSuccess) e = moe::launch_combine(q, yp, inv, w, y, s0);
+  if (e == hipSuccess) e = moe::launch_combine(q, yp, inv, fold ? nullptr : w, y, s0);
   return hip_status(e, "moe_layer");
 }
 

@@ -71,8 +71,12 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
 /* flags */
 enum {
   MOE_F_WRITE_LOGITS = 1u, /* moe_layer: also write fp32 logits to routing_out->logits */
-  MOE_F_OVERLAP = 2u       /* moe_layer: pack the second half of the local experts on
+  MOE_F_OVERLAP = 2u,      /* moe_layer: pack the second half of the local experts on
                               stream2 while the first half's GEMMs run on stream */
+  MOE_F_FOLD_WEIGHT = 4u   /* moe_layer: apply each assignment's routing weight in the
+                              down projection's epilogue, y_packed[p] = rnd(w * (h W2)),
+                              and combine the rows unweighted (one rounding point moves;
+                              see moe_layer) */
 };
 
 /* Which call a workspace size is asked for. */
@@ -213,8 +217,9 @@ moe_status_t moe_expert_gemm(const moe_problem_t* p, const void* x_packed, const
  * over the unpadded or the padded layout (y_packed rows are read at inv),
  *   y[t] = rnd(sum over j < k with inv[t*k+j] >= 0 of topk_w[t,j] * y_packed[inv[t*k+j]])
  * accumulated in fp32 in slot order.  A token with no local slot gets an exact
- * zero row; every row of y is written.
- *   y_packed [rows_max,d] dtype;  inv [T*k];  topk_w [T,k] fp32;  y [T,d] dtype
+ * zero row; every row of y is written.  topk_w = NULL sums the rows with unit
+ * weights (rows that already carry their weight, as MOE_F_FOLD_WEIGHT makes).
+ *   y_packed [rows_max,d] dtype;  inv [T*k];  topk_w [T,k] fp32 or NULL;  y [T,d] dtype
  */
 moe_status_t moe_combine(const moe_problem_t* p, const void* y_packed, const int32_t* inv,
                          const float* topk_w, void* y, void* stream);
@@ -297,12 +302,28 @@ moe_status_t moe_tile_forward(int32_t M, int32_t N, const void* C, void* dst, co
  * non-NULL stream2, the row gather of the upper half of the local experts runs
  * on stream2 while the lower half's GEMMs run on `stream` (the two-stream
  * dispatch overlap of CUCo, Abstract and Table 4); stream2 is joined back into
- * `stream` before the call returns its work.
+ * `stream` before the call returns its work.  With MOE_F_FOLD_WEIGHT the
+ * routing weight of each local assignment scales its expert output row before
+ * that row is rounded (y_packed[p] = rnd(w[perm[p]] * (h[p] W2_e))) and the
+ * combine sums rows unweighted, y[t] = rnd(sum of the token's local rows): the
+ * same value in exact arithmetic, with the gate weight applied where the pages'
+ * fused epilogues would apply it (CUCo, Table 4, row "MoE Dispatch/Combine").
  */
 moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate,
                        const float* bias, const void* w1, const void* w3, const void* w2,
                        void* y, const moe_routing_out_t* routing_out, void* workspace,
                        size_t workspace_bytes, void* stream, void* stream2);
+
+/*
+ * Byte offset, inside a moe_layer workspace for problem p, of an intermediate
+ * the layer leaves there: MOE_WS_H (h [rows_max,f]) or MOE_WS_Y_PACKED
+ * (y_packed [rows_max,d]), in the problem dtype; after a moe_layer call the
+ * first A rows hold that call's values (with MOE_F_FOLD_WEIGHT, y_packed rows
+ * carry their weights).  For inspecting a layer stage by stage; (size_t)-1 for
+ * an invalid p, an empty batch or an unknown region.
+ */
+enum { MOE_WS_H = 0, MOE_WS_Y_PACKED = 1 };
+size_t moe_layer_ws_offset(const moe_problem_t* p, int32_t what);
 
 #ifdef __cplusplus
 }

@@ -241,3 +241,21 @@ def test_dispatch_noalloc_rejects_oversize():
                                   None) == M.MOE_ERR_INVALID_ARG       # perm is NULL
     assert b"perm is NULL" in L.moe_last_error()
 
+
+def test_layer_ws_offset_and_fold_flag():
+    """The layer workspace's h and y_packed offsets lie inside it, 256-byte
+    aligned, y_packed after h; unknown regions and empty batches are errors;
+    MOE_F_FOLD_WEIGHT is a valid flag."""
+    L = M.lib()
+    p = M.Problem(300, 128, 16, 4, 64, 0, 8, M.MOE_DTYPE_BF16, M.MOE_F_FOLD_WEIGHT)
+    total = L.moe_workspace_bytes(ctypes.byref(p), M.MOE_CALL_LAYER)
+    assert total > 0 and L.moe_last_error() == b""
+    oh = L.moe_layer_ws_offset(ctypes.byref(p), M.MOE_WS_H)
+    oy = L.moe_layer_ws_offset(ctypes.byref(p), M.MOE_WS_Y_PACKED)
+    rows = 300 * 4
+    assert oh % 256 == 0 and oy % 256 == 0
+    assert oh + rows * 64 * 2 <= oy and oy + rows * 128 * 2 <= total
+    bad = ctypes.c_size_t(-1).value
+    assert L.moe_layer_ws_offset(ctypes.byref(p), 7) == bad and b"region" in L.moe_last_error()
+    empty = M.Problem(0, 128, 16, 4, 64, 0, 8, M.MOE_DTYPE_BF16, 0)
+    assert L.moe_layer_ws_offset(ctypes.byref(empty), M.MOE_WS_H) == bad

@@ -138,3 +138,50 @@ def test_layer_full_size(name):
     print(f"[full-size] {name}: A={A} stage errors h {eh:.3e} y_packed {ey:.3e} y {e_y:.3e}"
           f" (bar {STAGE_TOL[w.dtype]:g})", flush=True)
     print(f"[full-size] {name}: " + _chained_report(w, inp, gi, gw, yg, inv2, frac), flush=True)
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "dsv3_prefill_skew", "dense8_prefill"])
+def test_layer_fold_weight_full_size(name):
+    """The layer with the routing weights folded into the down projection, at
+    full size, stage by stage from the layer's own workspace: h on the
+    gathered rows, the weighted y_packed on the GPU's h and weights, y (an
+    unweighted sum) on the GPU's y_packed; every stage within one bf16 step
+    (on dense8, h and y_packed on a seeded quarter of each expert's rows)."""
+    import torch
+    w = workloads.get(name)
+    print(f"[full-size fold] {name}: generating", flush=True)
+    inp = workloads.generate(w)
+    d = {k: dev(v) for k, v in inp.items()}
+    p = M.Spec.of(w)
+    ws = M.alloc_workspace(M.Spec.of(w, M.MOE_F_FOLD_WEIGHT))
+    y, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True,
+                   fold_weight=True, workspace=ws)
+    torch.cuda.synchronize()
+    gi, gw = host(r["topk_idx"]), host(r["topk_w"])
+    counts, offsets, perm, inv = O.local_dispatch(gi, w.E, w.expert_lo, w.n_local)
+    assert np.array_equal(host(r["offsets"]), offsets)
+    A = int(offsets[-1])
+    assert np.array_equal(host(r["perm"])[:A], perm)
+    u16 = ws.view(torch.int16)
+    oh, oy = M.layer_ws_offset(p, M.MOE_WS_H), M.layer_ws_offset(p, M.MOE_WS_Y_PACKED)
+    hg = O.widen(u16[oh // 2: oh // 2 + A * w.f].cpu().numpy().view(np.uint16).reshape(A, w.f), w.dtype)
+    ypg = O.widen(u16[oy // 2: oy // 2 + A * w.d].cpu().numpy().view(np.uint16).reshape(A, w.d), w.dtype)
+    yh = host(y)
+    del d, ws
+    torch.cuda.empty_cache()
+    frac = SAMPLED.get(name)
+    rows, soff = (np.arange(A), offsets) if frac is None else _sample_rows(offsets, frac)
+    xp = O.gather_rows(inp["x"], perm, w.k)
+    hr, _ = O.swiglu_experts(xp[rows], soff, inp["w1"], inp["w3"], inp["w2"], w.dtype)
+    eh = check_close(hg[rows], hr, w.dtype, "h (oracle on the gathered rows)", STAGE_TOL[w.dtype])
+    del hr
+    scale = gw.astype(np.float64).ravel()[perm.astype(np.int64)]
+    ypr = O.down_projection(hg[rows], soff, inp["w2"], w.dtype, row_scale=scale[rows])
+    ey = check_close(ypg[rows], ypr, w.dtype, "weighted y_packed (oracle on the GPU's h)",
+                     STAGE_TOL[w.dtype])
+    del ypr
+    yr = O.combine(ypg, inv, None, w.dtype, k=w.k)
+    e_y = check_close(O.widen(yh, w.dtype), yr, w.dtype, "y (oracle sum of the GPU's rows)",
+                      STAGE_TOL[w.dtype])
+    print(f"[full-size fold] {name}: A={A} stage errors h {eh:.3e} y_packed {ey:.3e} y {e_y:.3e}",
+          flush=True)

@@ -223,6 +223,40 @@ def test_layer(name, overlap):
     check_close(O.widen(host(y), w.dtype), oref["y"], w.dtype, "y")
 
 
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_fold_weight(name):
+    """Routing weights folded into the down projection (MOE_F_FOLD_WEIGHT):
+    routing and dispatch as the plain layer, y against the oracle's folded
+    layer (y_packed[p] = rnd(w (h W2)), unweighted combine) on the GPU's
+    routing; also with the two-stream overlap."""
+    import torch
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    for overlap in (False, True):
+        s2 = torch.cuda.Stream() if overlap else None
+        y, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True,
+                       fold_weight=True, overlap=overlap, stream2=s2)
+        torch.cuda.synchronize()
+        routing = {"topk_idx": host(r["topk_idx"]), "topk_w": host(r["topk_w"])}
+        oref = O.moe_layer(w, inp, routing=routing, fold_weight=True)
+        assert np.array_equal(host(r["offsets"]), oref["offsets"])
+        A = int(oref["offsets"][-1])
+        assert np.array_equal(host(r["perm"])[:A], oref["perm"])
+        check_close(O.widen(host(y), w.dtype), oref["y"], w.dtype, f"y folded (overlap={overlap})")
+
+
+@pytest.mark.parametrize("name", ["wide_dsv3_like", "many_slots_k16", "fp32_mid", "skew"])
+def test_combine_unweighted(name):
+    """combine with no weights sums the local rows in slot order."""
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, d["x"])
+    y = host(M.combine(p, o["x_packed"], o["inv"], None))
+    yr = O.combine(O.widen(host(o["x_packed"]), w.dtype), host(o["inv"]), None, w.dtype, k=w.k)
+    check_close(O.widen(y, w.dtype), yr, w.dtype, "unweighted combine")
+
+
 # padded fixed-capacity layout (the A/B against the unpadded segments)
 PADDED = ["skew", "narrow_multiblock", "mixed_classes", "big_mixed", "fp32_mid", "one_local"]
 
