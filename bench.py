@@ -132,7 +132,46 @@ def write_traffic(a):
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
+    kernel_traffic_table(a, n)
     print(json.dumps(out))
+
+
+def _kname(k: str) -> str:
+    """Demangled kernel name without its return type, namespace and arguments."""
+    k = k.replace("(anonymous namespace)::", "").split("(")[0]
+    return k.replace("void ", "").replace("moe::", "").strip()
+
+
+def kernel_traffic_table(a, n):
+    """Every kernel of the same two counter runs: mean scaled FETCH_SIZE and
+    WRITE_SIZE bytes per dispatch, as a markdown table under profiles/."""
+    per = {}
+    for cname, d in (("FETCH_SIZE", a.write_traffic[0]), ("WRITE_SIZE", a.write_traffic[1])):
+        rows = _pmc_rows(d)
+        scale = n / (max(v for k, v in rows if "copyBuffer" in k) * 1024.0)
+        for k, v in rows:
+            if "at::native" in k or "fillBuffer" in k:   # the harness's own fills and flushes
+                continue
+            per.setdefault(_kname(k), {}).setdefault(cname, []).append(v * 1024.0 * scale)
+    lines = [f"# HBM traffic per kernel dispatch: {a.workload}", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 runs,",
+             f"each scaled by bytes moved / counter for the {a.copy_gib:g} GiB device copy",
+             "that bench.py runs in the same process; mean over the run's dispatches.",
+             "Commands (from /tmp with TMPDIR=/tmp, paths relative to the repo root):", "", "```"]
+    lines += [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py "
+              f"--workload {a.workload} --steps 3 --warmup 1 --no-cpu-baseline"
+              for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    lines += [f"python3 bench.py --workload {a.workload} --write-traffic <fetch dir> <write dir>",
+              "```", "", "| kernel | dispatches | read MB | write MB | total MB |", "|---|---|---|---|---|"]
+    for k in sorted(per):
+        f, w = per[k].get("FETCH_SIZE", []), per[k].get("WRITE_SIZE", [])
+        mf = sum(f) / len(f) if f else 0.0
+        mw = sum(w) / len(w) if w else 0.0
+        lines.append(f"| `{k}` | {max(len(f), len(w))} | {mf / 1e6:.3f} | {mw / 1e6:.3f} | "
+                     f"{(mf + mw) / 1e6:.3f} |")
+    path = os.path.join(ROOT, "profiles", f"traffic_kernels_{a.workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def hip_clock_mhz():
@@ -517,8 +556,6 @@ def main():
         return torch.from_numpy(x).cuda()
 
     torch.cuda.set_device(0)
-    copy = copy_bandwidth(a.copy_gib) if a.copy_gib > 0 else None
-    rd = read_ceiling(a.copy_gib) if a.copy_gib > 0 else None
     d = {k: dev(v) for k, v in inp.items()}
     p = M.Spec.of(w, M.MOE_F_OVERLAP if a.overlap else 0)
     stream = torch.cuda.current_stream()
@@ -539,6 +576,11 @@ def main():
     A = int(offsets[-1])
     active = int((counts > 0).sum())
 
+    # the HBM ceilings (untimed context figures) run here, after the weight
+    # upload over PCIe has left the GPU idle, so that the warm-up steps start
+    # from a busy device rather than from idle clocks
+    copy = copy_bandwidth(a.copy_gib) if a.copy_gib > 0 else None
+    rd = read_ceiling(a.copy_gib) if a.copy_gib > 0 else None
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
