@@ -7,10 +7,15 @@
 // into LDS with 16-byte-per-lane load-to-LDS instructions, so no register
 // holds the data in transit and no instruction rewrites it.  Each weight copy
 // instruction reads two 512-byte runs of rows of B (long runs keep the load
-// pipe of a compute unit near its streaming rate).  Three LDS slots form a
-// ring: two stages are in flight while the third is multiplied.  A stage is
-// released by an explicit wait for the wave's own copies (vmcnt) and one
-// barrier.
+// pipe of a compute unit near its streaming rate).  The weights and the A
+// rows have rings of their own: four weight slots (three stages in flight
+// while the fourth is multiplied) and three A slots (two in flight), 159 KB of
+// LDS in all.  A wave's copies retire in issue order, so a copy's wait budget
+// ends at the first later copy that some stage needs; issuing each step's A
+// copies (stage st + 2) before its weight copies (stage st + 3) gives the
+// weights, which come from HBM, three steps and the A rows, mostly L2 hits,
+// two.  A stage is released by an explicit wait for the wave's own copies
+// (vmcnt) and one barrier.
 //
 // The MFMA runs with the weights as its 16-row operand: a lane's fragment, 8
 // consecutive k of one weight column, comes from two ds_read_b64_tr_b16 reads
@@ -39,9 +44,15 @@ constexpr int DT_MT = 5;                     // m-tiles per row half at most
 constexpr int DT_BM = 32 * DT_MT;            // rows per tile at most
 constexpr int DT_BN = 512;                   // weight columns per tile
 constexpr int DT_PANEL = DT_KS * 256 * 2;    // bytes of one 256-column panel stage
-constexpr int DT_AOFF = 2 * DT_PANEL;        // A rows follow the two panels
-constexpr int DT_DUMMY = DT_AOFF + DT_BM * DT_KS * 2;  // 1 KB target of the unused A copies
-constexpr int DT_SLOT = DT_DUMMY + 1024;              // bytes per ring slot
+constexpr int DT_WSLOT = 2 * DT_PANEL;       // bytes of a weight stage (two panels)
+constexpr int DT_ASLOT = DT_BM * DT_KS * 2;  // bytes of an A stage
+constexpr int DT_NWS = 4;                    // weight slots
+constexpr int DT_NAS = 3;                    // A slots
+constexpr int DT_AREG = DT_NWS * DT_WSLOT;   // the A slots follow the weight slots
+constexpr int DT_DUMMY = DT_AREG + DT_NAS * DT_ASLOT;  // 1 KB target of the unused A copies
+constexpr int DT_LDS = DT_DUMMY + 1024;                // bytes of LDS the ring takes
+static_assert((DT_NWS & (DT_NWS - 1)) == 0, "weight slots rotate by a mask");
+static_assert(DT_LDS <= 160 * 1024, "the ring fits the LDS of a compute unit");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -72,14 +83,10 @@ __device__ __forceinline__ s16x4 dt_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((dt_lds4_t*)p);
 }
 
-constexpr int DT_AI = (2 * DT_MT + 7) / 8;   // A copy instructions per wave per stage, at most
-
-// The three ring slots (distinct __shared__ arrays of DT_SLOT bytes) and a
-// table of DT_AI * 512 words for the lanes' A copy offsets (each lane reads
-// back only the entries it wrote, so the table needs no barrier).
+// The ring: one __shared__ array of DT_LDS bytes (weight slot j at j DT_WSLOT,
+// A slot j at DT_AREG + j DT_ASLOT).
 struct DtSlots {
-  char* s[3];
-  uint32_t* tab;
+  char* ring;
 };
 
 // Weight panel row j (0..31) stores source piece q (16 bytes) at piece
@@ -94,8 +101,9 @@ __device__ __forceinline__ int dt_swa(int r) { return ((r >> 1) & 3) ^ ((r >> 3)
 template <int MT>
 struct DtCtx {
   static constexpr int AI = (2 * MT + 7) / 8;   // A copy instructions per wave per stage
-  static constexpr int CNT = 4 + AI;            // copy instructions per stage, every wave
+  static constexpr int CW = 4;                  // weight copy instructions per wave per stage
   __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[AI];   // A copies: lane source offsets (bytes) at stage K column 0
   uint32_t vb[2];    // weight copies 0, 1: lane source offsets (bytes) at stage K row 0;
                      // copies 2, 3 read 4 rows further with the same offsets
   uint32_t ldb2;     // bytes per row of B
@@ -106,20 +114,25 @@ struct DtCtx {
                      // t of a panel is at wx ^ (32 t) (plus DT_PANEL for GEMM-1's W3)
 };
 
-// Stage st into slot J: 4 weight copies per wave, then its A copies.
-template <int J, int MT>
-__device__ __forceinline__ void dt_issue(const DtCtx<MT>& c, const DtSlots& S, int st) {
-  char* slot = S.s[J];
-  const uint32_t k0 = (uint32_t)(st * DT_KS);
-  const uint32_t sb = k0 * c.ldb2;
+// The weights of stage st into the weight slot at byte offset wo: 4 copies per wave.
+template <int MT>
+__device__ __forceinline__ void dt_issue_w(const DtCtx<MT>& c, const DtSlots& S, uint32_t wo, int st) {
+  char* slot = S.ring + wo;
+  const uint32_t sb = (uint32_t)(st * DT_KS) * c.ldb2;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     dt_copy16(c.rb, slot + c.bdst + 1024 * u, c.vb[u & 1], sb + (u >> 1) * 4 * c.ldb2);
+}
+
+// The A rows of stage st into the A slot at byte offset ao: AI copies per wave.
+template <int MT>
+__device__ __forceinline__ void dt_issue_a(const DtCtx<MT>& c, const DtSlots& S, uint32_t ao, int st) {
+  char* slot = S.ring + ao;
 #pragma unroll
   for (int v = 0; v < DtCtx<MT>::AI; ++v) {
     const int a = c.wave + 8 * v;
-    dt_copy16(c.ra, slot + (a < 2 * MT ? DT_AOFF + 1024 * a : DT_DUMMY), S.tab[512 * v + threadIdx.x],
-              k0 * 2);
+    dt_copy16(c.ra, a < 2 * MT ? slot + 1024 * a : S.ring + DT_DUMMY, c.va[v],
+              (uint32_t)(st * DT_KS * 2));
   }
 }
 
@@ -129,12 +142,14 @@ __device__ __forceinline__ void dt_sync() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Multiply the stage in slot J.  kleft < DT_KS (last stage only, MASK) zeroes
-// both fragments for k past the end, whatever the slot holds there.
-template <int J, bool MASK, bool SWIGLU, int MT>
-__device__ __forceinline__ void dt_compute(const DtCtx<MT>& c, const DtSlots& S, int kleft,
-                                           f32x4 (&acc)[MT][8]) {
-  const char* slot = S.s[J];
+// Multiply the stage in the weight slot at wo and the A slot at ao.  kleft <
+// DT_KS (last stage only, MASK) zeroes both fragments for k past the end,
+// whatever the slots hold there.
+template <bool MASK, bool SWIGLU, int MT>
+__device__ __forceinline__ void dt_compute(const DtCtx<MT>& c, const DtSlots& S, uint32_t wo,
+                                           uint32_t ao, int kleft, f32x4 (&acc)[MT][8]) {
+  const char* slot = S.ring + wo;
+  const char* aslot = S.ring + ao;
   const int g = (threadIdx.x & 63) >> 4;
   const bool zero = MASK && 8 * g >= kleft;
   // the per-tile offsets are one XOR each; recomputing them every stage keeps
@@ -145,7 +160,7 @@ __device__ __forceinline__ void dt_compute(const DtCtx<MT>& c, const DtSlots& S,
   bf16x8 xf[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    xf[mt] = *reinterpret_cast<const bf16x8*>(slot + DT_AOFF + c.aoff + 1024 * mt);
+    xf[mt] = *reinterpret_cast<const bf16x8*>(aslot + c.aoff + 1024 * mt);
     if (zero) xf[mt] = bf16x8{};
   }
 #pragma unroll
@@ -170,26 +185,17 @@ __device__ __forceinline__ void dt_compute(const DtCtx<MT>& c, const DtSlots& S,
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Stage st in slot J = st % 3: wait for it, refill the slot of stage st - 1
-// (every wave is past it) with stage st + 2, multiply.  GUARD: the form with
-// range conditions (tail).  (Refilling a slot right after its own multiply,
-// behind a second barrier, keeps three stages in flight but puts the multiply
-// on the critical path; it measured slower.)
-template <int J, bool GUARD, bool SWIGLU, int MT>
-__device__ __forceinline__ void dt_step(const DtCtx<MT>& c, const DtSlots& S, int st, int nst, int K,
-                                        f32x4 (&acc)[MT][8]) {
-  if (GUARD && st >= nst) return;
-  if (!GUARD || st + 1 < nst) dt_sync<DtCtx<MT>::CNT>();
-  else dt_sync<0>();
-  if (!GUARD || st + 2 < nst) dt_issue<(J + 2) % 3>(c, S, st + 2);
-  dt_compute<J, GUARD, SWIGLU>(c, S, K - st * DT_KS, acc);
-}
-
-template <int J, bool GUARD, bool SWIGLU, int MT>
-__device__ __forceinline__ void dt_trip(const DtCtx<MT>& c, const DtSlots& S, int st, int nst, int K,
-                                        f32x4 (&acc)[MT][8]) {
-  dt_step<J, GUARD, SWIGLU>(c, S, st + J, nst, K, acc);
-  if constexpr (J < 2) dt_trip<J + 1, GUARD, SWIGLU>(c, S, st, nst, K, acc);
+// One step: wait for stage st (NW: this wave's copies that may stay in
+// flight), refill the slots of stage st - 1 (every wave is past them) with
+// the A rows of stage st + 2 (IA) and the weights of stage st + 3 (IW),
+// multiply stage st.
+template <int NW, bool IA, bool IW, bool MASK, bool SWIGLU, int MT>
+__device__ __forceinline__ void dt_step(const DtCtx<MT>& c, const DtSlots& S, int st, uint32_t wo,
+                                        uint32_t ao, int K, f32x4 (&acc)[MT][8]) {
+  dt_sync<NW>();
+  if constexpr (IA) dt_issue_a(c, S, DT_AREG + (ao == DT_AREG ? 2 * DT_ASLOT : ao - DT_AREG - DT_ASLOT), st + 2);
+  if constexpr (IW) dt_issue_w(c, S, (wo + (DT_NWS - 1) * DT_WSLOT) & (DT_NWS * DT_WSLOT - 1), st + 3);
+  dt_compute<MASK, SWIGLU>(c, S, wo, ao, K - st * DT_KS, acc);
 }
 
 // One medium block: rows [r0, r0 + R) of expert e (32 (MT - 1) < R <= 32 MT,
@@ -228,16 +234,15 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
     c.vb[u] = col < cend ? (uint32_t)(((int64_t)j * N + col) * 2) : GC_OOR;
   }
   c.bdst = panel * DT_PANEL + 4096 * (wave & 3);
-  // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row.
-  // The lane source offsets (bytes, below 2^31: the A descriptor's size) go to
-  // the table: across the K loop they would need registers.
+  // A copies: instruction a covers tile rows 16 a .. 16 a + 15, 4 lanes a row
+  // (lane source offsets in bytes, below 2^31: the A descriptor's size).
   c.ra = rows ? gc_rsrc(A, abytes) : gc_rsrc(A + (int64_t)r0 * K, (uint32_t)((int64_t)R * K * 2));
 #pragma unroll
   for (int v = 0; v < DtCtx<MT>::AI; ++v) {
     const int r = 16 * (wave + 8 * v) + (lane >> 2);
     const int rr = min(r, R - 1);
     const uint32_t row = rows ? (uint32_t)(rows[r0 + rr] / rdiv) : (uint32_t)rr;
-    S.tab[512 * v + threadIdx.x] = wave + 8 * v < 2 * MT
+    c.va[v] = wave + 8 * v < 2 * MT
         ? (row * (uint32_t)K + 8u * (uint32_t)((lane & 3) ^ dt_swa(r))) * 2u
         : GC_OOR;
   }
@@ -257,14 +262,42 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
   for (int a = 0; a < MT; ++a)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Copies in issue order: W0 A0 W1 A1 W2, then per step st A(st + 2) W(st + 3).
+  // The wait of step st needs A(st) (and W(st), issued before it); after A(st)
+  // come W(st + 1), A(st + 1) and W(st + 2), those of them that exist.
+  constexpr int CW = DtCtx<MT>::CW, CA = DtCtx<MT>::AI;
   const int nst = (K + DT_KS - 1) / DT_KS;
   if (nst > 0) {
-    dt_issue<0>(c, S, 0);
-    if (nst > 1) dt_issue<1>(c, S, 1);
+    dt_issue_w(c, S, 0, 0);
+    dt_issue_a(c, S, DT_AREG, 0);
+    if (nst > 1) {
+      dt_issue_w(c, S, DT_WSLOT, 1);
+      dt_issue_a(c, S, DT_AREG + DT_ASLOT, 1);
+    }
+    if (nst > 2) dt_issue_w(c, S, 2 * DT_WSLOT, 2);
+    // wave-uniform slot offsets of stage st
+    uint32_t wo = 0, ao = DT_AREG;
     int st = 0;
-    for (; st + 5 <= nst; st += 3) dt_trip<0, false, SWIGLU>(c, S, st, nst, K, acc);
-    dt_trip<0, true, SWIGLU>(c, S, st, nst, K, acc);
-    dt_trip<0, true, SWIGLU>(c, S, st + 3, nst, K, acc);
+    for (; st + 3 < nst; ++st) {
+      dt_step<2 * CW + CA, true, true, false, SWIGLU>(c, S, st, wo, ao, K, acc);
+      wo = (wo + DT_WSLOT) & (DT_NWS * DT_WSLOT - 1);
+      ao = ao == DT_AREG + 2 * DT_ASLOT ? DT_AREG : ao + DT_ASLOT;
+    }
+    // the last min(nst, 3) stages; only the last one can be partial in K (its
+    // masked form zeroes nothing when it is whole: one form, no branch)
+    if (st + 2 < nst) {
+      dt_step<2 * CW + CA, true, false, false, SWIGLU>(c, S, st, wo, ao, K, acc);
+      wo = (wo + DT_WSLOT) & (DT_NWS * DT_WSLOT - 1);
+      ao = ao == DT_AREG + 2 * DT_ASLOT ? DT_AREG : ao + DT_ASLOT;
+      ++st;
+    }
+    if (st + 1 < nst) {
+      dt_step<CW + CA, false, false, false, SWIGLU>(c, S, st, wo, ao, K, acc);
+      wo = (wo + DT_WSLOT) & (DT_NWS * DT_WSLOT - 1);
+      ao = ao == DT_AREG + 2 * DT_ASLOT ? DT_AREG : ao + DT_ASLOT;
+      ++st;
+    }
+    dt_step<0, false, false, true, SWIGLU>(c, S, st, wo, ao, K, acc);
   }
 
   // epilogue: lane (i, g), m-tile mt, n-tile t holds row 16 MT wm + 16 mt + i,

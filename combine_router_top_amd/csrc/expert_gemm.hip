@@ -19,9 +19,9 @@
 //     the same W3 columns; after the K loop the upper half passes its products
 //     to the lower half through LDS, which applies SiLU(x.W1)*(x.W3).
 //   medium (up to XM_BM rows per block, prefill): both operands are copied
-//     from memory straight into a 3-slot LDS ring and multiplied with the
-//     weights as the MFMA row operand (dma_tile.h); W1 and W3 products of an
-//     h column meet in one register.
+//     from memory straight into LDS rings (four weight slots, three A
+//     slots) and multiplied with the weights as the MFMA row operand
+//     (dma_tile.h); W1 and W3 products of an h column meet in one register.
 // The row-block schedule is derived on the device from `offsets` in the
 // workgroup prologue, so the number of local assignments never travels to the
 // host; the grid is sized for the worst case and surplus workgroups exit
@@ -368,11 +368,15 @@ __device__ BigTile big_tile_at(int L, const int32_t* __restrict__ offsets, int e
 }
 
 static_assert(XGThin::NW == 8, "one workgroup size for all streamed tile classes");
-// The thin tiles borrow the medium ring slots: the A stages in slot 0, the
-// W3 -> W1 accumulator exchange in slots 1 and 2 (half of the pairs each).
-static_assert(2 * gc_lds_elems<XGThin::NW, XGThin::CPL, XGThin::MTMAX>() <= DT_SLOT,
-              "thin A stages fit one slot");
-static_assert(XGThin::XCH / 2 * 4 <= DT_SLOT, "half of the thin exchange fits one slot");
+// The thin tiles borrow the medium ring: the A stages in its first third, the
+// W3 -> W1 accumulator exchange in the other two (half of the pairs each).
+// The schedule's prefix sums sit at the start of the ring until the row block
+// is known.
+constexpr int XG_TPART = DT_LDS / 3 / 16 * 16;
+static_assert(2 * gc_lds_elems<XGThin::NW, XGThin::CPL, XGThin::MTMAX>() <= XG_TPART,
+              "thin A stages fit a third of the ring");
+static_assert(XGThin::XCH / 2 * 4 <= XG_TPART, "half of the thin exchange fits a third of the ring");
+static_assert(2 * (XG_MAXN + 1) * 4 <= DT_LDS, "the schedule's prefix sums fit the ring");
 
 // SWIGLU: A = x_packed [*, K = d], B1/B3 = w1/w3 [n][K][N = f], C = h [*, f]
 // else:   A = h [*, K = f], B1 = w2 [n][K][N = d], C = y_packed [*, d]
@@ -387,14 +391,11 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
                                                                      int K, int N,
                                                                      bf16_t* __restrict__ C, int th,
                                                                      int mcols, int tcols, RowMap rm) {
-  __shared__ __attribute__((aligned(16))) char S0[DT_SLOT];
-  __shared__ __attribute__((aligned(16))) char S1[DT_SLOT];
-  __shared__ __attribute__((aligned(16))) char S2[DT_SLOT];
-  __shared__ uint32_t dtab[DT_AI * 512];
-  __shared__ int pre[2 * (XG_MAXN + 1)];
+  __shared__ __attribute__((aligned(16))) char ring[DT_LDS];
   // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
   const int ncols = SWIGLU ? 2 * N : N;
-  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, mcols, SWIGLU ? XGThin::COLS : tcols, pre);
+  RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, mcols, SWIGLU ? XGThin::COLS : tcols,
+                         reinterpret_cast<int*>(ring));
   // values from LDS and the wave index are wave-uniform; say so, so that
   // pointers and buffer descriptors built from them live in scalar registers
   rb.e = __builtin_amdgcn_readfirstlane(rb.e);
@@ -402,15 +403,16 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
   rb.R = __builtin_amdgcn_readfirstlane(rb.R);
   rb.nb = __builtin_amdgcn_readfirstlane(rb.nb);
   rb.cls = __builtin_amdgcn_readfirstlane(rb.cls);
-  if (rb.R <= 0) return;
+  if (rb.R <= 0) return;   // uniform over the workgroup
+  __syncthreads();         // every wave has read the prefix sums before the ring is written
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (rb.cls == 0) {
     stream_block<XGThin, SWIGLU>(A, B1, B3, K, N, C, rb, rm, wave, SWIGLU ? XGThin::COLS : tcols,
-                                 reinterpret_cast<bf16_t*>(S0), reinterpret_cast<float*>(S1),
-                                 reinterpret_cast<float*>(S2));
+                                 reinterpret_cast<bf16_t*>(ring), reinterpret_cast<float*>(ring + XG_TPART),
+                                 reinterpret_cast<float*>(ring + 2 * XG_TPART));
     return;
   }
-  const DtSlots slots{{S0, S1, S2}, dtab};
+  const DtSlots slots{ring};
   switch ((rb.R + 31) >> 5) {
 #define XM_CASE(n)                                                                              \
   case n:                                                                                       \
