@@ -628,10 +628,14 @@ def main():
     h = torch.empty((w.rows_max, w.f), dtype=y.dtype, device="cuda")
     yp = torch.empty((w.rows_max, w.d), dtype=y.dtype, device="cuda")
     names = ["route", "dispatch", "expert_gemm", "combine"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     tot = {n: 0.0 for n in names}
     iters = max(5, a.steps)
+    # all iterations are enqueued before one synchronisation, so the launch
+    # stream runs ahead of the device and no call's time includes its own
+    # host-side launch (an event recorded on an idle device would count it)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters + 2)]
     for it in range(iters + 2):
+        ev = evs[it]
         ev[0].record(stream)
         M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt))
         ev[1].record(stream)
@@ -641,10 +645,11 @@ def main():
         ev[3].record(stream)
         M.combine(p, yp, dsp["inv"], wt, out=y)
         ev[4].record(stream)
-        torch.cuda.synchronize()
-        if it >= 2:
-            for j, n in enumerate(names):
-                tot[n] += ev[j].elapsed_time(ev[j + 1])
+    torch.cuda.synchronize()
+    for it in range(2, iters + 2):
+        for j, n in enumerate(names):
+            tot[n] += evs[it][j].elapsed_time(evs[it][j + 1])
+    ev = evs[0]
     # the same calls cold: before each, a read pass over 1 GiB evicts the L2s
     # and the 256 MB MALL, so every operand comes from HBM.  The pass only
     # reads, so the caches it leaves hold clean lines: a fill instead would

@@ -103,16 +103,27 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     __syncthreads();
   }
 
-  // 1. per local expert: total count and count in the chunks before this one
+  // this chunk's expert ids, loaded first so that their round trip overlaps
+  // the histogram reads below
+  const int64_t wbeg = (int64_t)c * DCH + wave * 256;
+  int key[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t a = wbeg + r * 64 + lane;
+    key[r] = a < TK ? idx[a] : -1;
+  }
+
+  // 1. per expert (all E: workgroup 0 also writes the global counts): total
+  // count, and for the local experts the count in the chunks before this one
   // (DUN independent loads in flight per round instead of one round trip per chunk)
-  for (int e = tid; e < n; e += 256) {
+  for (int ge = tid; ge < E; ge += 256) {
     int tot = 0, pre = 0;
     int cc = ONE ? nchunks : 0;
-    if constexpr (ONE) tot = hl[lo + e];
+    if constexpr (ONE) tot = hl[ge];
     for (; cc + DUN <= nchunks; cc += DUN) {
       int v[DUN];
 #pragma unroll
-      for (int u = 0; u < DUN; ++u) v[u] = chunk_hist[(int64_t)(cc + u) * E + lo + e];
+      for (int u = 0; u < DUN; ++u) v[u] = chunk_hist[(int64_t)(cc + u) * E + ge];
 #pragma unroll
       for (int u = 0; u < DUN; ++u) {
         pre += cc + u < c ? v[u] : 0;
@@ -120,12 +131,16 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
       }
     }
     for (; cc < nchunks; ++cc) {
-      const int v = chunk_hist[(int64_t)cc * E + lo + e];
+      const int v = chunk_hist[(int64_t)cc * E + ge];
       pre += cc < c ? v : 0;
       tot += v;
     }
-    base[e] = tot;
-    wpos[0][e] = pre;
+    if (c == 0) counts_all[ge] = tot;
+    const int e = ge - lo;
+    if ((unsigned)e < (unsigned)n) {
+      base[e] = tot;
+      wpos[0][e] = pre;
+    }
   }
   __syncthreads();
 
@@ -148,36 +163,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     }
     run += v4[q];
   }
-  if (c == 0) {
-    if (tid == 0) offsets[n] = total;
-    for (int e = tid; e < E; e += 256) {
-      int t = 0;
-      int cc = ONE ? nchunks : 0;
-      if constexpr (ONE) t = hl[e];
-      for (; cc + DUN <= nchunks; cc += DUN) {
-        int v[DUN];
-#pragma unroll
-        for (int u = 0; u < DUN; ++u) v[u] = chunk_hist[(int64_t)(cc + u) * E + e];
-#pragma unroll
-        for (int u = 0; u < DUN; ++u) t += v[u];
-      }
-      for (; cc < nchunks; ++cc) t += chunk_hist[(int64_t)cc * E + e];
-      counts_all[e] = t;
-    }
-  }
+  if (c == 0 && tid == 0) offsets[n] = total;
   __syncthreads();
 
   // 3. per-wave counts of local experts over the wave's 256 assignments
   for (int e = lane; e < n; e += 64) wpos[wave][e] = 0;
   __syncthreads();
-  const int64_t wbeg = (int64_t)c * DCH + wave * 256;
-  int key[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int64_t a = wbeg + r * 64 + lane;
-    int e = -1;
-    if (a < TK) {
-      e = idx[a] - lo;
+    int e = key[r];
+    if (e >= 0) {
+      e -= lo;
       if ((unsigned)e >= (unsigned)n) e = -1;
     }
     key[r] = e;

@@ -300,25 +300,48 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
     dt_step<0, false, false, true, SWIGLU>(c, S, st, wo, ao, K, acc);
   }
 
-  // epilogue: lane (i, g), m-tile mt, n-tile t holds row 16 MT wm + 16 mt + i,
-  // columns 16 t + 4 g .. + 3 of the wave's column range
+  // Epilogue: lane (i, g), m-tile mt, n-tile t holds row 16 MT wm + 16 mt + i,
+  // columns 16 t + 4 g .. + 3 of the wave's WC columns.  Stored as they lie,
+  // each instruction would write 16 rows x 32 bytes; instead each m-tile goes
+  // through a wave-private 16-row LDS tile and leaves as whole row runs of the
+  // wave's columns (16 bytes a lane, 128 or 256 bytes a row), several times
+  // fewer and longer write requests.  The tile's 32-byte chunks are XOR-
+  // swizzled by row so that the 8-byte writes of 16 rows spread over the banks.
+  constexpr int WC = SWIGLU ? 64 : 128;   // output columns per wave
+  constexpr int RB = 2 * WC;              // bytes per staged row
+  constexpr int NCH = RB / 32;            // 32-byte chunks per staged row
+  constexpr int LPR = RB / 16;            // lanes per row in the read-back
+  constexpr int RPI = 64 / LPR;           // rows per read-back instruction
+  __syncthreads();                        // every wave is past the ring's last stage
+  char* stg = S.ring + 4096 * wave;
+  const int colw = cblk + WC * wn;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int row = 16 * MT * wm + 16 * mt + i;
-    const float sc = !SWIGLU && rscale && row < R ? rscale[r0 + row] : 1.0f;
+    const int rbase = 16 * MT * wm + 16 * mt;
+    const float sc = !SWIGLU && rscale && rbase + i < R ? rscale[r0 + rbase + i] : 1.0f;
 #pragma unroll
-    for (int t = 0; t < (SWIGLU ? 4 : 8); ++t) {
-      const int col = cblk + (SWIGLU ? 64 * wn : 128 * wn) + 16 * t + 4 * g;
+    for (int t = 0; t < WC / 16; ++t) {
       float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acc[mt][t][r];
         o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a * sc;
       }
-      if (row < R && col < cend)
-        *reinterpret_cast<u32x2*>(C + (int64_t)(r0 + row) * N + col) =
-            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(stg + i * RB + 32 * (t ^ (i & (NCH - 1))) + 8 * g) =
+          u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 16 / RPI; ++q) {
+      const int row = RPI * q + lane / LPR;
+      const int p = lane % LPR;   // 16-byte piece of the row: columns 8 p .. 8 p + 7
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * RB + 32 * ((p >> 1) ^ (row & (NCH - 1))) +
+                                                      16 * (p & 1));
+      const int col = colw + 8 * p;
+      if (rbase + row < R && col < cend)
+        *reinterpret_cast<u32x4*>(C + (int64_t)(r0 + rbase + row) * N + col) = v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
