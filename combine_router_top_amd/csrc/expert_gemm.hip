@@ -112,6 +112,37 @@ __device__ __forceinline__ int xg_blocks(int cnt, int th, int ncols, int cls, in
   return (cnt + XM_BM - 1) / XM_BM * ((ncols + mcols - 1) / mcols);
 }
 
+// Real workgroups per XCD of a streamed launch with these parameters: the
+// number of blocks that start in XCD x's window of schedule() below, i.e.
+// min(first(w1), blocks) - first(w0) with first(w) the first block starting
+// at or after w.  Wave 0 of the calling workgroup; lane x < 8 writes cnt[x].
+// GEMM-1 writes them for GEMM-2, whose surplus workgroups (the grid covers
+// the worst routing) then exit after one load instead of the schedule.
+__device__ void xg_xcd_counts(const int32_t* __restrict__ offsets, int e_begin, int e_end, int th,
+                              int ncols, int mcols, int tcols, int* __restrict__ cnt) {
+  const int lane = threadIdx.x & 63;
+  const int ne = e_end - e_begin;
+  int nth = 0, nwd = 0;
+  for (int j = lane; j < ne; j += 64) {
+    const int c = offsets[e_begin + j + 1] - offsets[e_begin + j];
+    nth += xg_blocks(c, th, ncols, 0, mcols, tcols);
+    nwd += xg_blocks(c, th, ncols, 1, mcols, tcols);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    nth += __shfl_xor(nth, off);
+    nwd += __shfl_xor(nwd, off);
+  }
+  if (lane < 8) {
+    const int wm = mcols / XG_WUNIT, wt = tcols / XG_WUNIT;
+    const int wth = wt * nth, W = wth + wm * nwd;
+    const int w0 = (lane * W + 7) >> 3, w1 = ((lane + 1) * W + 7) >> 3;
+    const int f0 = w0 <= wth ? (w0 + wt - 1) / wt : nth + (w0 - wth + wm - 1) / wm;
+    const int f1 = w1 <= wth ? (w1 + wt - 1) / wt : nth + (w1 - wth + wm - 1) / wm;
+    cnt[lane] = max(0, min(f1, nth + nwd) - f0);
+  }
+}
+
 // Schedule from `offsets` (computed by every workgroup, a few hundred cycles).
 // Experts in [e_begin, e_end) with fewer than `th` rows contribute (row block,
 // column block) pairs of their tile class.  The blocks are listed thin class
@@ -390,8 +421,19 @@ __global__ __launch_bounds__(64 * XGThin::NW) void grouped_gemm_bf16(const bf16_
                                                                      const bf16_t* __restrict__ B3,
                                                                      int K, int N,
                                                                      bf16_t* __restrict__ C, int th,
-                                                                     int mcols, int tcols, RowMap rm) {
+                                                                     int mcols, int tcols, RowMap rm,
+                                                                     int* __restrict__ xcnt, int ncols2,
+                                                                     int mcols2, int tcols2) {
   __shared__ __attribute__((aligned(16))) char ring[DT_LDS];
+  // xcnt (or NULL): GEMM-1's workgroup 0 writes the down projection's real
+  // workgroups per XCD (ncols2 output columns, mcols2 / tcols2 block widths);
+  // the down projection's surplus workgroups leave at once
+  if constexpr (SWIGLU) {
+    if (xcnt && blockIdx.x == 0 && threadIdx.x < 64)
+      xg_xcd_counts(offsets, e_begin, e_end, th, ncols2, mcols2, tcols2, xcnt);
+  } else {
+    if (xcnt && (int)(blockIdx.x >> 3) >= xcnt[blockIdx.x & 7]) return;
+  }
   // GEMM-1 is counted in weight columns: each workgroup streams the columns of W1 and of W3
   const int ncols = SWIGLU ? 2 * N : N;
   RowBlock rb = schedule(offsets, e_begin, e_end, th, ncols, mcols, SWIGLU ? XGThin::COLS : tcols,
@@ -585,11 +627,12 @@ static int big_cus() {
   return n;
 }
 
-size_t expert_gemm_ws_bytes(const Prob&) { return 0; }
+// the down projection's real workgroups per XCD (8 ints), written by GEMM-1
+size_t expert_gemm_ws_bytes(const Prob& p) { return p.dtype == 1 ? 256 : 0; }
 
 hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t* offsets,
                               const void* w1, const void* w3, const void* w2, void* h,
-                              void* y_packed, void*, int e_begin, int e_end, hipStream_t st,
+                              void* y_packed, void* ws, int e_begin, int e_end, hipStream_t st,
                               const int32_t* perm, const float* rscale) {
   if (p.rows_max == 0 || e_end <= e_begin) return hipSuccess;
   if (p.dtype == 1) {
@@ -676,9 +719,10 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
                          (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, ntn, rm1);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    int* xcnt = reinterpret_cast<int*>(ws);
     hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid(2 * p.f, mc1, tc1)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)x_packed, offsets, e_begin, e_end, (const bf16_t*)w1,
-                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, mc1, tc1, rm1);
+                       (const bf16_t*)w3, p.d, p.f, (bf16_t*)h, th, mc1, tc1, rm1, xcnt, p.d, mc2, tc2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (big) {
       const int ntn = (p.d + 255) / 256;
@@ -689,7 +733,8 @@ hipError_t launch_expert_gemm(const Prob& p, const void* x_packed, const int32_t
     }
     hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid(p.d, mc2, tc2)), dim3(64 * XGThin::NW), 0, st,
                        (const bf16_t*)h, offsets, e_begin, e_end, (const bf16_t*)w2,
-                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, mc2, tc2, rm2);
+                       (const bf16_t*)nullptr, p.f, p.d, (bf16_t*)y_packed, th, mc2, tc2, rm2, xcnt,
+                       0, 0, 0);
     return hipGetLastError();
   }
   dim3 g1((unsigned)p.rows_max, (p.f + 255) / 256);
