@@ -174,6 +174,35 @@ def kernel_traffic_table(a, n):
         fh.write("\n".join(lines) + "\n")
 
 
+class HipEvents:
+    """Raw HIP events (timing enabled) for the library to record itself."""
+
+    def __init__(self, n):
+        import ctypes
+        self._c = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self._hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: hipError {rc}")
+            self.ev.append(h.value)
+
+    def elapsed_ms(self, i, j) -> float:
+        ms = self._c.c_float(0.0)
+        rc = self._hip.hipEventElapsedTime(self._c.byref(ms), self._c.c_void_p(self.ev[i]),
+                                           self._c.c_void_p(self.ev[j]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: hipError {rc}")
+        return ms.value
+
+    def close(self):
+        for h in self.ev:
+            self._hip.hipEventDestroy(self._c.c_void_p(h))
+        self.ev = []
+
+
 def hip_clock_mhz():
     """Peak clock the HIP runtime reports for device 0 (hipDeviceAttributeClockRate,
     value 5 in ROCm 7's hip_runtime_api.h, in kHz), or None."""
@@ -577,7 +606,8 @@ def main():
     active = int((counts > 0).sum())
 
     # The untimed context figures run before the warm-up: the HBM ceilings,
-    # then each ABI call on its own.  After the weight upload over PCIe the
+    # then each ABI call on its own, cold (after a cache-evicting read) and
+    # then warm, so that the contract's steps follow warm work.  After the weight upload over PCIe the
     # first few dozen layer steps run 5-10% slower than the steady state (a
     # 20-step block right after 5 warm-up steps: 0.64-0.67 ms against 0.60);
     # these calls carry the device through that before the contract's W
@@ -595,33 +625,12 @@ def main():
     h = torch.empty((w.rows_max, w.f), dtype=y.dtype, device="cuda")
     yp = torch.empty((w.rows_max, w.d), dtype=y.dtype, device="cuda")
     names = ["route", "dispatch", "expert_gemm", "combine"]
-    tot = {n: 0.0 for n in names}
-    iters = max(5, a.steps)
-    # all iterations are enqueued before one synchronisation, so the launch
-    # stream runs ahead of the device and no call's time includes its own
-    # host-side launch (an event recorded on an idle device would count it)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters + 2)]
-    for it in range(iters + 2):
-        ev = evs[it]
-        ev[0].record(stream)
-        M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt))
-        ev[1].record(stream)
-        M.dispatch(p, idx, d["x"], workspace=ws_d, out=dsp)
-        ev[2].record(stream)
-        M.expert_gemm(p, dsp["x_packed"], dsp["offsets"], d["w1"], d["w3"], d["w2"], out=(h, yp))
-        ev[3].record(stream)
-        M.combine(p, yp, dsp["inv"], wt, out=y)
-        ev[4].record(stream)
-    torch.cuda.synchronize()
-    for it in range(2, iters + 2):
-        for j, n in enumerate(names):
-            tot[n] += evs[it][j].elapsed_time(evs[it][j + 1])
-    ev = evs[0]
     # the same calls cold: before each, a read pass over 1 GiB evicts the L2s
     # and the 256 MB MALL, so every operand comes from HBM.  The pass only
     # reads, so the caches it leaves hold clean lines: a fill instead would
     # leave 256 MB of dirty lines whose write-back the next call would pay for.
     flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     cold = {n: 0.0 for n in names}
     calls = [
         lambda: M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt)),
@@ -640,19 +649,53 @@ def main():
             if it >= 1:
                 cold[n] += ev[0].elapsed_time(ev[1])
     del flush
+    tot = {n: 0.0 for n in names}
+    iters = max(5, a.steps)
+    # all iterations are enqueued before one synchronisation, so the launch
+    # stream runs ahead of the device and no call's time includes its own
+    # host-side launch (an event recorded on an idle device would count it).
+    # The first SKIP iterations are not counted: after the cold calls, whose
+    # flushes and synchronisations leave the device idle between calls, the
+    # first few dozen calls run slower than the steady state.
+    SKIP = 20
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters + SKIP)]
+    for it in range(iters + SKIP):
+        ev = evs[it]
+        ev[0].record(stream)
+        M.route(p, d["x"], d["w_gate"], d["bias"], workspace=ws_r, out=(idx, wt))
+        ev[1].record(stream)
+        M.dispatch(p, idx, d["x"], workspace=ws_d, out=dsp)
+        ev[2].record(stream)
+        M.expert_gemm(p, dsp["x_packed"], dsp["offsets"], d["w1"], d["w3"], d["w2"], out=(h, yp))
+        ev[3].record(stream)
+        M.combine(p, yp, dsp["inv"], wt, out=y)
+        ev[4].record(stream)
+    torch.cuda.synchronize()
+    for it in range(SKIP, iters + SKIP):
+        for j, n in enumerate(names):
+            tot[n] += evs[it][j].elapsed_time(evs[it][j + 1])
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events the layer records around its expert GEMM in every timed step
+    # (the plain path; the overlap path splits the GEMM and records none)
+    gev = HipEvents(2 * a.steps) if not a.overlap else None
     w0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(a.steps):
+    for i in range(a.steps):
+        if gev:
+            M.layer_set_gemm_events(gev.ev[2 * i], gev.ev[2 * i + 1])
         step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / a.steps
+    gemm_in_step = None
+    if gev:
+        gemm_in_step = float(np.mean([gev.elapsed_ms(2 * i, 2 * i + 1) for i in range(a.steps)]))
+        gev.close()
     # step-time distribution: the same number of steps again, an event after each
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     sev[0].record(stream)
@@ -693,10 +736,19 @@ def main():
     phases = {n: phase(n, tot[n] / iters / 1e3) for n in names}
     phases_cold = {n: phase(n, cold[n] / cold_iters / 1e3) for n in names}
 
-    g = phases["expert_gemm"]
+    # the dominant unit: the expert GEMM launches inside the timed layer steps
+    # (HIP events on the launch stream around them, averaged over the K steps);
+    # without them (overlap path), the same call timed on its own
+    if gemm_in_step is not None:
+        g = phase("expert_gemm", gemm_in_step / 1e3)
+        where = "inside the timed moe_layer steps"
+    else:
+        g = phases["expert_gemm"]
+        where = "moe_expert_gemm timed on its own"
     roof = {k: g[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roof["kernel"] = ("moe_expert_gemm: grouped_gemm_bf16<SwiGLU> + grouped_gemm_bf16<down> "
-                      "(+ the two large-tile launches when segments reach 320 rows)")
+    roof["kernel"] = ("expert GEMM: grouped_gemm_bf16<SwiGLU> + grouped_gemm_bf16<down> "
+                      "(+ the two large-tile launches when segments reach 320 rows), " + where)
+    roof["us_per_launch_pair"] = g["ms"] * 1e3
     roof["traffic"] = committed_traffic(w.name)
     roof["algorithmic_bytes"] = model["expert_gemm"]["bytes"]
     roof["algorithmic_flops"] = model["expert_gemm"]["flops"]

@@ -41,7 +41,7 @@ MOE_SCOPE_AGENT, MOE_SCOPE_SYSTEM = 0, 1
 EXPORTED = ["moe_last_error", "moe_version", "moe_workspace_bytes", "moe_route", "moe_dispatch",
             "moe_expert_gemm", "moe_combine", "moe_layer", "moe_dispatch_padded",
             "moe_expert_gemm_padded", "moe_gemm_signal_tiles", "moe_gemm_signal", "moe_tile_forward",
-            "moe_dispatch_noalloc", "moe_layer_ws_offset"]
+            "moe_dispatch_noalloc", "moe_layer_ws_offset", "moe_layer_set_gemm_events"]
 
 
 class MoeError(RuntimeError):
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_layer_ws_offset.argtypes = [P, i32]
         L.moe_layer_ws_offset.restype = sz
+        L.moe_layer_set_gemm_events.argtypes = [vp, vp]
         L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -384,6 +385,13 @@ def tile_forward(C, dst, flags, epoch: int, spin_limit: int, timeouts, workgroup
                                   int(spin_limit), int(scope), _ptr(timeouts), int(workgroups),
                                   _stream(stream)))
     return dst
+
+
+def layer_set_gemm_events(before: int, after: int) -> None:
+    """The next layer() call on this thread records the two HIP events (raw
+    hipEvent_t handles, timing enabled) on its launch stream around its expert
+    GEMM."""
+    _check(lib().moe_layer_set_gemm_events(ctypes.c_void_p(before or 0), ctypes.c_void_p(after or 0)))
 
 
 def layer_ws_offset(p: Spec, what: int) -> int:

@@ -196,6 +196,16 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 
 const char* moe_version(void) { return "libmoe 0.2 gfx950"; }
 
+// events the next moe_layer call on this thread records around its expert GEMM
+thread_local hipEvent_t g_gemm_ev[2] = {nullptr, nullptr};
+
+moe_status_t moe_layer_set_gemm_events(void* before, void* after) {
+  g_gemm_ev[0] = reinterpret_cast<hipEvent_t>(before);
+  g_gemm_ev[1] = reinterpret_cast<hipEvent_t>(after);
+  g_err.clear();
+  return MOE_OK;
+}
+
 size_t moe_layer_ws_offset(const moe_problem_t* p, int32_t what) {
   moe::Prob q;
   if (check_problem(p, &q) != MOE_OK) return (size_t)-1;
@@ -461,6 +471,9 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
                        const float* bias, const void* w1, const void* w3, const void* w2,
                        void* y, const moe_routing_out_t* routing_out, void* workspace,
                        size_t workspace_bytes, void* stream, void* stream2) {
+  // the measurement hook is consumed by this call whatever its outcome
+  const hipEvent_t ev_before = g_gemm_ev[0], ev_after = g_gemm_ev[1];
+  g_gemm_ev[0] = g_gemm_ev[1] = nullptr;
   moe::Prob q;
   moe_status_t st = check_problem(p, &q);
   if (st != MOE_OK) return st;
@@ -529,10 +542,13 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
   // itself through perm, so x_packed is never written
   const bool fused = q.dtype == 1 && (int64_t)q.T * q.d * 2 < (int64_t(1) << 31);
   if (!overlap && fused) {
-    e = moe::launch_expert_gemm(q, x, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0, perm,
+    if (ev_before) e = hipEventRecord(ev_before, s0);
+    if (e == hipSuccess)
+      e = moe::launch_expert_gemm(q, x, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0, perm,
                                 rscale);
   } else if (!overlap) {
     e = moe::launch_gather(q, x, offsets, perm, xp, 0, q.n, s0);
+    if (e == hipSuccess && ev_before) e = hipEventRecord(ev_before, s0);
     if (e == hipSuccess)
       e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, 0, q.n, s0,
                                   nullptr, rscale);
@@ -554,6 +570,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
       e = moe::launch_expert_gemm(q, xp, offsets, w1, w3, w2, h, yp, ws + L.gemm, half, q.n, s0,
                                   nullptr, rscale);
   }
+  if (e == hipSuccess && ev_after && !overlap) e = hipEventRecord(ev_after, s0);
   if (e == hipSuccess) e = moe::launch_combine(q, yp, inv, fold ? nullptr : w, y, s0);
   return hip_status(e, "moe_layer");
 }

@@ -325,6 +325,15 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const void* w_gate
 enum { MOE_WS_H = 0, MOE_WS_Y_PACKED = 1 };
 size_t moe_layer_ws_offset(const moe_problem_t* p, int32_t what);
 
+/*
+ * Measurement hook: the next moe_layer call on this host thread records the
+ * HIP events `before` and `after` (hipEvent_t, created by the caller) on its
+ * launch stream immediately before and after its expert-GEMM launches, so that
+ * a benchmark can time the grouped GEMM inside the layer step it times.  The
+ * hook is consumed by that call; NULL events record nothing.  Returns MOE_OK.
+ */
+moe_status_t moe_layer_set_gemm_events(void* before, void* after);
+
 #ifdef __cplusplus
 }
 #endif
