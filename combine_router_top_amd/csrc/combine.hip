@@ -9,7 +9,9 @@
 // into LDS; each lane then owns two 16-byte pieces of the chunk and loads them
 // for up to 8 slots at once before accumulating them in slot order, so a
 // token with k local slots costs one round trip per 8 slots, and a short
-// batch (decode) still spreads over T x ceil(d / 1024) waves.
+// batch (decode) still spreads over T x ceil(d / 1024) waves.  y is stored
+// non-temporally: the layer does not read it again, and left dirty in the
+// MALL it would be written back while the next layer's weights stream in.
 #include "common.h"
 #include "kernels.h"
 
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[u][q]);
     }
-    dst[v] = o;
+    __builtin_nontemporal_store(o, dst + v);
   }
 }
 

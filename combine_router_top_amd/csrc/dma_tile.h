@@ -307,6 +307,11 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
   // wave's columns (16 bytes a lane, 128 or 256 bytes a row), several times
   // fewer and longer write requests.  The tile's 32-byte chunks are XOR-
   // swizzled by row so that the 8-byte writes of 16 rows spread over the banks.
+  // The stores are non-temporal: h and y_packed are each read once, by the
+  // next launch, and left dirty in the MALL they would be written back while
+  // the next step's weight stream evicts them.  (Only whole row runs go out
+  // this way: non-temporal 32-byte pieces, as the large and thin tiles store
+  // them, miss the L2's write combining and cost more than they save.)
   constexpr int WC = SWIGLU ? 64 : 128;   // output columns per wave
   constexpr int RB = 2 * WC;              // bytes per staged row
   constexpr int NCH = RB / 32;            // 32-byte chunks per staged row
@@ -339,7 +344,7 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
                                                       16 * (p & 1));
       const int col = colw + 8 * p;
       if (rbase + row < R && col < cend)
-        *reinterpret_cast<u32x4*>(C + (int64_t)(r0 + rbase + row) * N + col) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (int64_t)(r0 + rbase + row) * N + col));
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }

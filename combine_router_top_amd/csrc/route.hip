@@ -87,8 +87,9 @@ __global__ __launch_bounds__(64 * RW_NW) void router_wide_mfma(const bf16_t* __r
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * mt + 4 * g + r;
       if (row < R) {
-        f32x2 v = f32x2{acc[mt][0][r], acc[mt][1][r]};
-        *reinterpret_cast<f32x2*>(out + (int64_t)(m0 + row) * E + col) = v;
+        // read once by top-k: streamed past the caches (non-temporal)
+        __builtin_nontemporal_store(f32x2{acc[mt][0][r], acc[mt][1][r]},
+                                    reinterpret_cast<f32x2*>(out + (int64_t)(m0 + row) * E + col));
       }
     }
 }
@@ -269,7 +270,8 @@ __global__ __launch_bounds__(512, 1) void router_dma(const bf16_t* __restrict__ 
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int col = cb * RD_BN + 64 * wn + 16 * t + 4 * g;
-      if (row < R && col < E) *reinterpret_cast<f32x4*>(out + (int64_t)row * E + col) = acc[mt][t];
+      if (row < R && col < E)   // read once by top-k: non-temporal
+        __builtin_nontemporal_store(acc[mt][t], reinterpret_cast<f32x4*>(out + (int64_t)row * E + col));
     }
   }
   if (zero)
