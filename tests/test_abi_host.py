@@ -259,3 +259,9 @@ def test_layer_ws_offset_and_fold_flag():
     assert L.moe_layer_ws_offset(ctypes.byref(p), 7) == bad and b"region" in L.moe_last_error()
     empty = M.Problem(0, 128, 16, 4, 64, 0, 8, M.MOE_DTYPE_BF16, 0)
     assert L.moe_layer_ws_offset(ctypes.byref(empty), M.MOE_WS_H) == bad
+
+
+def test_layer_gemm_events_hook_host():
+    """The measurement hook takes NULL events (records nothing) and needs no GPU."""
+    assert M.lib().moe_layer_set_gemm_events(None, None) == M.MOE_OK
+    M.layer_set_gemm_events(0, 0)

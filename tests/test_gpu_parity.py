@@ -324,6 +324,46 @@ def test_layer_deterministic_and_overlap_identical():
             assert np.array_equal(outs[0][k], o[k]), k
 
 
+def test_layer_gemm_events_hook():
+    """The measurement hook: the next moe_layer call records the two events
+    around its expert GEMM (a positive interval inside the call's own), the
+    output is unchanged, and the hook is consumed by that call."""
+    import ctypes
+    import torch
+    w, inp, ref, d = case("wide_dsv3_like")
+    p = M.Spec.of(w)
+    hip = ctypes.CDLL("libamdhip64.so")
+    ev = []
+    for _ in range(4):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        ev.append(h.value)
+    try:
+        y0 = host(M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"]))
+        st = torch.cuda.current_stream()
+        assert hip.hipEventRecord(ctypes.c_void_p(ev[0]), ctypes.c_void_p(st.cuda_stream)) == 0
+        M.layer_set_gemm_events(ev[1], ev[2])
+        y1 = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], stream=st)
+        assert hip.hipEventRecord(ctypes.c_void_p(ev[3]), ctypes.c_void_p(st.cuda_stream)) == 0
+        torch.cuda.synchronize()
+        ms = []
+        for a, b in ((0, 3), (1, 2)):
+            t = ctypes.c_float(0.0)
+            assert hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(ev[a]), ctypes.c_void_p(ev[b])) == 0
+            ms.append(t.value)
+        assert 0.0 < ms[1] <= ms[0], ms
+        assert np.array_equal(host(y1), y0)
+        # consumed: a second call records nothing new (the events keep their times)
+        M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], stream=st)
+        torch.cuda.synchronize()
+        t = ctypes.c_float(0.0)
+        assert hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(ev[1]), ctypes.c_void_p(ev[2])) == 0
+        assert t.value == ms[1]
+    finally:
+        for h in ev:
+            hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
 @pytest.mark.parametrize("name", ["wide_dsv3_like", "narrow_multiblock", "fp32_mid"])
 def test_layer_token_shuffle_equivariance(name):
     """Permuting tokens permutes routing and outputs; bit-exact because each
