@@ -262,17 +262,29 @@ __global__ __launch_bounds__(512, 1) void router_dma(const bf16_t* __restrict__ 
   }
 
   // lane (i, g) of m-tile mt, n-tile t: token 64 wm + 16 mt + i, experts
-  // 64 wn + 16 t + 4 g .. + 3 of the block
-  float* out = part + ((int64_t)split * T + m0) * E;
+  // 64 wn + 16 t + 4 g .. + 3 of the block.  The partials are read once, by
+  // top-k, so they are stored non-temporally; to leave as whole 1 KB rows
+  // (non-temporal 64-byte pieces miss the L2's write combining: 1.5x the
+  // bytes at the memory) the block goes through the idle ring first, 16-byte
+  // pieces XOR-swizzled by row so that a 16-row write spreads over the banks.
+  static_assert(RD_BM * RD_BN * 4 <= 3 * RD_SLOT, "the partial block fits the ring");
+  __syncthreads();   // every wave is past the last stage
+  float* stg = reinterpret_cast<float*>(ring);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int row = 64 * wm + 16 * mt + i;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int col = cb * RD_BN + 64 * wn + 16 * t + 4 * g;
-      if (row < R && col < E)   // read once by top-k: non-temporal
-        __builtin_nontemporal_store(acc[mt][t], reinterpret_cast<f32x4*>(out + (int64_t)row * E + col));
+      const int piece = (16 * wn + 4 * t + g) ^ (row & 15);   // 16-byte piece of the 1 KB row
+      *reinterpret_cast<f32x4*>(stg + row * RD_BN + 4 * piece) = acc[mt][t];
     }
+  }
+  __syncthreads();
+  float* out = part + ((int64_t)split * T + m0) * E;
+  const int col = cb * RD_BN + 4 * lane;
+  for (int row = wave; row < R; row += 8) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * RD_BN + 4 * (lane ^ (row & 15)));
+    if (col < E) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + (int64_t)row * E + col));
   }
   if (zero)
     for (int q = b * 512 + (int)threadIdx.x; q < nzero; q += gridDim.x * 512) zero[q] = 0;
