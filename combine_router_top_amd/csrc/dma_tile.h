@@ -49,8 +49,7 @@ constexpr int DT_ASLOT = DT_BM * DT_KS * 2;  // bytes of an A stage
 constexpr int DT_NWS = 4;                    // weight slots
 constexpr int DT_NAS = 3;                    // A slots
 constexpr int DT_AREG = DT_NWS * DT_WSLOT;   // the A slots follow the weight slots
-constexpr int DT_DUMMY = DT_AREG + DT_NAS * DT_ASLOT;  // 1 KB target of the unused A copies
-constexpr int DT_LDS = DT_DUMMY + 1024;                // bytes of LDS the ring takes
+constexpr int DT_LDS = DT_AREG + DT_NAS * DT_ASLOT;    // bytes of LDS the ring takes
 static_assert((DT_NWS & (DT_NWS - 1)) == 0, "weight slots rotate by a mask");
 static_assert(DT_LDS <= 160 * 1024, "the ring fits the LDS of a compute unit");
 
@@ -94,13 +93,15 @@ struct DtSlots {
 __device__ __forceinline__ int dt_swb(int j) { return 2 * ((j & 3) | (((j >> 3) & 1) << 2)); }
 __device__ __forceinline__ int dt_swa(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-// Every wave issues the same copies per stage (4 weight copies, AI A copies),
-// without branches: waves past the last A instruction copy from an offset
-// outside the A descriptor (nothing is fetched) into the slot's dummy area.
-// The per-stage count is then exact for the vmcnt waits.
+// Per stage every wave issues 4 weight copies and the first AFULL waves AI A
+// copies, the others AI - 1: a copy instruction costs the compute unit's
+// address unit its time whether or not it fetches anything, so a tile with
+// fewer than 8 AI A instructions issues no padding copies.  The per-stage
+// count of each wave is then exact for its vmcnt waits.
 template <int MT>
 struct DtCtx {
-  static constexpr int AI = (2 * MT + 7) / 8;   // A copy instructions per wave per stage
+  static constexpr int AI = (2 * MT + 7) / 8;   // A copy instructions per wave per stage, at most
+  static constexpr int AFULL = 2 * MT - 8 * (AI - 1);  // waves with AI of them
   static constexpr int CW = 4;                  // weight copy instructions per wave per stage
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va[AI];   // A copies: lane source offsets (bytes) at stage K column 0
@@ -109,6 +110,7 @@ struct DtCtx {
   uint32_t ldb2;     // bytes per row of B
   int bdst;          // this wave's first weight destination inside a slot (bytes)
   int wave;
+  bool afull;        // wave < AFULL (wave-uniform)
   int aoff;          // lane's A fragment offset inside the A region (m-tile 0)
   int wx;            // lane's weight fragment offset of the wave's first n-tile; n-tile
                      // t of a panel is at wx ^ (32 t) (plus DT_PANEL for GEMM-1's W3)
@@ -124,15 +126,15 @@ __device__ __forceinline__ void dt_issue_w(const DtCtx<MT>& c, const DtSlots& S,
     dt_copy16(c.rb, slot + c.bdst + 1024 * u, c.vb[u & 1], sb + (u >> 1) * 4 * c.ldb2);
 }
 
-// The A rows of stage st into the A slot at byte offset ao: AI copies per wave.
+// The A rows of stage st into the A slot at byte offset ao: AI or AI - 1
+// copies per wave (instruction a = wave + 8 v covers rows 16 a .. 16 a + 15).
 template <int MT>
 __device__ __forceinline__ void dt_issue_a(const DtCtx<MT>& c, const DtSlots& S, uint32_t ao, int st) {
   char* slot = S.ring + ao;
 #pragma unroll
   for (int v = 0; v < DtCtx<MT>::AI; ++v) {
-    const int a = c.wave + 8 * v;
-    dt_copy16(c.ra, a < 2 * MT ? slot + 1024 * a : S.ring + DT_DUMMY, c.va[v],
-              (uint32_t)(st * DT_KS * 2));
+    const int a = c.wave + 8 * v;   // wave-uniform
+    if (a < 2 * MT) dt_copy16(c.ra, slot + 1024 * a, c.va[v], (uint32_t)(st * DT_KS * 2));
   }
 }
 
@@ -185,14 +187,16 @@ __device__ __forceinline__ void dt_compute(const DtCtx<MT>& c, const DtSlots& S,
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One step: wait for stage st (NW: this wave's copies that may stay in
-// flight), refill the slots of stage st - 1 (every wave is past them) with
-// the A rows of stage st + 2 (IA) and the weights of stage st + 3 (IW),
-// multiply stage st.
-template <int NW, bool IA, bool IW, bool MASK, bool SWIGLU, int MT>
+// One step: wait for stage st (KW stages of weight copies and KA of A copies
+// may stay in flight), refill the slots of stage st - 1 (every wave is past
+// them) with the A rows of stage st + 2 (IA) and the weights of stage st + 3
+// (IW), multiply stage st.
+template <int KW, int KA, bool IA, bool IW, bool MASK, bool SWIGLU, int MT>
 __device__ __forceinline__ void dt_step(const DtCtx<MT>& c, const DtSlots& S, int st, uint32_t wo,
                                         uint32_t ao, int K, f32x4 (&acc)[MT][8]) {
-  dt_sync<NW>();
+  constexpr int CW = DtCtx<MT>::CW, AI = DtCtx<MT>::AI;
+  if (c.afull) dt_sync<KW * CW + KA * AI>();
+  else dt_sync<KW * CW + KA * (AI - 1)>();
   if constexpr (IA) dt_issue_a(c, S, DT_AREG + (ao == DT_AREG ? 2 * DT_ASLOT : ao - DT_AREG - DT_ASLOT), st + 2);
   if constexpr (IW) dt_issue_w(c, S, (wo + (DT_NWS - 1) * DT_WSLOT) & (DT_NWS * DT_WSLOT - 1), st + 3);
   dt_compute<MASK, SWIGLU>(c, S, wo, ao, K - st * DT_KS, acc);
@@ -217,6 +221,7 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
   const int64_t estride = (int64_t)K * N;
   DtCtx<MT> c;
   c.wave = wave;
+  c.afull = wave < DtCtx<MT>::AFULL;
   // weight copies: waves 0-3 fill panel 0, waves 4-7 panel 1; wave w copies
   // panel rows 8 (w & 3) .. + 7, two rows per instruction
   const int panel = wave >> 2;
@@ -265,7 +270,6 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
   // Copies in issue order: W0 A0 W1 A1 W2, then per step st A(st + 2) W(st + 3).
   // The wait of step st needs A(st) (and W(st), issued before it); after A(st)
   // come W(st + 1), A(st + 1) and W(st + 2), those of them that exist.
-  constexpr int CW = DtCtx<MT>::CW, CA = DtCtx<MT>::AI;
   const int nst = (K + DT_KS - 1) / DT_KS;
   if (nst > 0) {
     dt_issue_w(c, S, 0, 0);
@@ -279,25 +283,25 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
     uint32_t wo = 0, ao = DT_AREG;
     int st = 0;
     for (; st + 3 < nst; ++st) {
-      dt_step<2 * CW + CA, true, true, false, SWIGLU>(c, S, st, wo, ao, K, acc);
+      dt_step<2, 1, true, true, false, SWIGLU>(c, S, st, wo, ao, K, acc);
       wo = (wo + DT_WSLOT) & (DT_NWS * DT_WSLOT - 1);
       ao = ao == DT_AREG + 2 * DT_ASLOT ? DT_AREG : ao + DT_ASLOT;
     }
     // the last min(nst, 3) stages; only the last one can be partial in K (its
     // masked form zeroes nothing when it is whole: one form, no branch)
     if (st + 2 < nst) {
-      dt_step<2 * CW + CA, true, false, false, SWIGLU>(c, S, st, wo, ao, K, acc);
+      dt_step<2, 1, true, false, false, SWIGLU>(c, S, st, wo, ao, K, acc);
       wo = (wo + DT_WSLOT) & (DT_NWS * DT_WSLOT - 1);
       ao = ao == DT_AREG + 2 * DT_ASLOT ? DT_AREG : ao + DT_ASLOT;
       ++st;
     }
     if (st + 1 < nst) {
-      dt_step<CW + CA, false, false, false, SWIGLU>(c, S, st, wo, ao, K, acc);
+      dt_step<1, 1, false, false, false, SWIGLU>(c, S, st, wo, ao, K, acc);
       wo = (wo + DT_WSLOT) & (DT_NWS * DT_WSLOT - 1);
       ao = ao == DT_AREG + 2 * DT_ASLOT ? DT_AREG : ao + DT_ASLOT;
       ++st;
     }
-    dt_step<0, false, false, true, SWIGLU>(c, S, st, wo, ao, K, acc);
+    dt_step<0, 0, false, false, true, SWIGLU>(c, S, st, wo, ao, K, acc);
   }
 
   // Epilogue: lane (i, g), m-tile mt, n-tile t holds row 16 MT wm + 16 mt + i,
