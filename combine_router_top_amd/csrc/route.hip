@@ -589,6 +589,80 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   topk_select<NV>(v, bias, logits_out, t, E, k, idx, w, hist);
 }
 
+// E a multiple of 4 in (192, 256] (4 values per lane): lane l holds the four
+// consecutive experts 4 l .. 4 l + 3, so each split's values for a token
+// arrive in one 16-byte load per lane, summed in ascending split order as in
+// topk_softmax_kernel.  Among lanes holding the round's maximum the lowest
+// lane holds the lowest expert index (and its own lowest slot among equal
+// keys), so ties need no second reduction.
+__global__ __launch_bounds__(256) void topk_softmax_vec4(const float* __restrict__ part, int nsplit,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ logits_out, int T, int E,
+                                                         int k, int32_t* __restrict__ idx,
+                                                         float* __restrict__ w,
+                                                         int32_t* __restrict__ hist) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int e0 = 4 * lane;
+  const bool valid = e0 < E;
+  // unconditional loads (lanes past E read the last quad), dropped below
+  const float* pt = part + (int64_t)t * E + (valid ? e0 : E - 4);
+  const int64_t sstride = (int64_t)T * E;
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; s += 8) {
+    f32x4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      q[u] = *reinterpret_cast<const f32x4*>(pt + (int64_t)min(s + u, nsplit - 1) * sstride);
+    v = s == 0 ? q[0] : v + q[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) v = s + u < nsplit ? v + q[u] : v;
+  }
+  uint32_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    key[j] = 0;
+    if (valid) {
+      float vj = v[j];
+      if (bias) vj += bias[e0 + j];
+      if (logits_out) logits_out[(int64_t)t * E + e0 + j] = vj;
+      key[j] = f32_order_key(vj);
+    }
+  }
+  uint32_t bk;
+  int bj;
+  lane_best<4>(key, bk, bj);
+  uint32_t myk = 0, k0 = 0;
+  int mye = 0;
+  for (int r = 0; r < k; ++r) {
+    const uint32_t m = wave_max_u32(bk);
+    const int L = (int)__builtin_ctzll(__ballot(bk == m));
+    const int jl = __builtin_amdgcn_readlane(bj, L);
+    const int e = 4 * L + jl;
+    if (r == 0) k0 = m;
+    if (lane == r) {
+      myk = m;
+      mye = e;
+    }
+    if (lane == L) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == jl) key[j] = 0;
+      lane_best<4>(key, bk, bj);
+    }
+  }
+  const float v0 = key_to_f32(k0);
+  const float ex = lane < k ? expf(key_to_f32(myk) - v0) : 0.f;
+  const float sum = wave_sum_f32(ex);
+  if (lane < k) {
+    const int64_t a = (int64_t)t * k + lane;
+    idx[a] = mye;
+    w[a] = ex / sum;
+    if (hist) atomicAdd(hist + (a >> 10) * E + mye, 1);
+  }
+}
+
 // Deep K splits (short batches): one workgroup per token, each of its 4 waves
 // sums a contiguous quarter of the splits (loads of up to 8 splits in flight
 // together), the quarters are added in wave order through LDS, and wave 0
@@ -743,6 +817,11 @@ hipError_t launch_route(const Prob& p, const void* x, const void* wg, const floa
                       : topk_softmax_multi<16>;
     hipLaunchKernelGGL(tk, dim3(p.T), dim3(256), 0, st, part, S, bias, logits, p.T, p.E, p.k, idx,
                        w, hist);
+    return hipGetLastError();
+  }
+  if (nv == 4 && p.E % 4 == 0) {
+    hipLaunchKernelGGL(topk_softmax_vec4, dim3((p.T + 3) / 4), dim3(256), 0, st, part, S, bias, logits,
+                       p.T, p.E, p.k, idx, w, hist);
     return hipGetLastError();
   }
   auto tk = nv <= 1 ? topk_softmax_kernel<1>

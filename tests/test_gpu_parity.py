@@ -79,6 +79,13 @@ SMALL = {
     # second with 64 valid experts
     "router_dma_tails": W("router_dma_tails", 1100, 1000, 256, 8, 64, 0, 32, "bf16", skew=True, seed=34),
     "router_dma_e320": W("router_dma_e320", 1030, 512, 320, 6, 48, 100, 40, "bf16", seed=35),
+    # the same router with one K split of two stages (64 + 32 of K) and of a
+    # single 40-deep stage: the pipelined loop's shortest forms
+    # top-k with four consecutive experts per lane and lanes past E idle
+    # (232 experts: lanes 58..63 hold none)
+    "topk_e232": W("topk_e232", 300, 256, 232, 8, 32, 40, 32, "bf16", seed=38),
+    "router_dma_k96": W("router_dma_k96", 1040, 96, 128, 4, 32, 0, 16, "bf16", seed=36),
+    "router_dma_k40": W("router_dma_k40", 1030, 40, 128, 2, 32, 8, 16, "bf16", seed=37),
     # medium GEMM-1 blocks of the full 512 weight columns at a small size
     # (64 experts x 1024 h columns, ~50 rows each: 256 blocks fill one round)
     "medium_w512": W("medium_w512", 1600, 64, 64, 2, 1024, 0, 64, "bf16", seed=28),
@@ -108,7 +115,8 @@ def test_route(name):
 @pytest.mark.parametrize("name", ["tiny_fp32", "wide_tails", "narrow_multiblock", "plain_router_bf16",
                                   "wide_ksplit", "wide_e20", "topk_e96",
                                   "topk_e384", "topk_e1024", "router_long", "topk_deep_e256",
-                                  "topk_deep_e1024", "router_dma_tails", "router_dma_e320"])
+                                  "topk_deep_e1024", "router_dma_tails", "router_dma_e320",
+                                  "router_dma_k96", "router_dma_k40", "topk_e232"])
 def test_route_integer_inputs_exact(name):
     """Small-integer x and W_g: logits are exact on both sides, so routing,
     including ties, must match with no exemption."""
