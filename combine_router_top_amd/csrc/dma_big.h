@@ -32,7 +32,8 @@
 // piece): half-panel row j keeps source piece q at q ^ 2 sigma(j), sigma(j) =
 // (j & 3) | ((j >> 3) & 1) << 2, so the 32 lanes of a transposing read (8 rows
 // x 32 bytes) cover all 64 banks once; A row r keeps piece q at q ^
-// dt_swa(r), so the 16 rows x 16 bytes of an A read do as well.
+// dt_swa(r), so that every pass of an A read meets 16 distinct 16-byte bank
+// groups (dma_tile.h).
 #pragma once
 
 #include "common.h"
