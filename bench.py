@@ -610,8 +610,9 @@ def main():
     # then warm, so that the contract's steps follow warm work.  After the weight upload over PCIe the
     # first few dozen layer steps run 5-10% slower than the steady state (a
     # 20-step block right after 5 warm-up steps: 0.64-0.67 ms against 0.60);
-    # these calls carry the device through that before the contract's W
-    # warm-up steps and K timed steps.
+    # these calls, and the step-time distribution and fold A/B below, carry
+    # the device through that before the contract's W warm-up steps and K
+    # timed steps.
     copy = copy_bandwidth(a.copy_gib) if a.copy_gib > 0 else None
     rd = read_ceiling(a.copy_gib) if a.copy_gib > 0 else None
 
@@ -675,28 +676,11 @@ def main():
         for j, n in enumerate(names):
             tot[n] += evs[it][j].elapsed_time(evs[it][j + 1])
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # events the layer records around its expert GEMM in every timed step
-    # (the plain path; the overlap path splits the GEMM and records none)
-    gev = HipEvents(2 * a.steps) if not a.overlap else None
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(a.steps):
-        if gev:
-            M.layer_set_gemm_events(gev.ev[2 * i], gev.ev[2 * i + 1])
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / a.steps
-    gemm_in_step = None
-    if gev:
-        gemm_in_step = float(np.mean([gev.elapsed_ms(2 * i, 2 * i + 1) for i in range(a.steps)]))
-        gev.close()
-    # step-time distribution: the same number of steps again, an event after each
+    # Layer-step measurements that the line reports besides the contract's
+    # mean; they run before the contract's W warm-up steps, so that those and
+    # the K timed steps follow a few dozen layer steps (the first layer steps
+    # after the per-call measurements run a few percent slower than later ones).
+    # step-time distribution: K steps, an event after each
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     sev[0].record(stream)
     for i in range(a.steps):
@@ -720,6 +704,28 @@ def main():
             torch.cuda.synchronize()
             fold_ab["fold_ms" if fold else "plain_ms"].append(f0.elapsed_time(f1) / a.steps)
     fold_ab = {k: float(np.median(v)) for k, v in fold_ab.items()}
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events the layer records around its expert GEMM in every timed step
+    # (the plain path; the overlap path splits the GEMM and records none)
+    gev = HipEvents(2 * a.steps) if not a.overlap else None
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(a.steps):
+        if gev:
+            M.layer_set_gemm_events(gev.ev[2 * i], gev.ev[2 * i + 1])
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / a.steps
+    gemm_in_step = None
+    if gev:
+        gemm_in_step = float(np.mean([gev.elapsed_ms(2 * i, 2 * i + 1) for i in range(a.steps)]))
+        gev.close()
 
 
     s = 2 if w.dtype == "bf16" else 4
