@@ -151,8 +151,9 @@ __device__ void xg_xcd_counts(const int32_t* __restrict__ offsets, int e_begin, 
 // weights before it.  XCD x (workgroup id mod 8 on this part) takes the blocks that start in
 // [ceil(x W / 8), ceil((x + 1) W / 8)) of the total work W, the q-th of them
 // going to its q-th workgroup.  Every XCD thus gets an equal share of the
-// weight stream, the column blocks of one row block mostly share one L2 for
-// their A rows, and within an XCD the longer thin blocks start first.  Block
+// weight stream, the blocks of one expert mostly share one L2 (an expert's
+// blocks go by column block, its row blocks fastest), and within an XCD the
+// longer thin blocks start first.  Block
 // starts are at least the smaller weight apart, so the grid needs
 // 8 ceil(ceil(W / 8) / min weight) workgroups at most.  R = 0 means "exit".
 // `pre` holds 2 (XG_MAXN + 1) ints.
@@ -208,10 +209,19 @@ __device__ RowBlock schedule(const int32_t* __restrict__ offsets, int e_begin, i
   const int o = offsets[e];
   const int cnt = offsets[e + 1] - o;
   const int bm = rb.cls ? XM_BM : XGThin::BM;
-  const int cols = rb.cls ? mcols : tcols;
-  const int nblk = (ncols + cols - 1) / cols;
-  const int jb = local / nblk;
-  rb.nb = local - jb * nblk;
+  // an expert's blocks in column-block order, its row blocks fastest: the
+  // row blocks of a long segment that run together on one XCD then share
+  // each weight column block in its L2 (with column blocks fastest only the
+  // two or so row blocks in flight did)
+  const int nrb = (cnt + bm - 1) / bm;
+  int jb;
+  if (nrb > 1) {
+    rb.nb = local / nrb;
+    jb = local - rb.nb * nrb;
+  } else {
+    jb = 0;
+    rb.nb = local;
+  }
   rb.e = e;
   rb.r0 = o + jb * bm;
   rb.R = min(bm, cnt - jb * bm);
