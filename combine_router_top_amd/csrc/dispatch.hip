@@ -30,7 +30,7 @@ namespace moe {
 
 constexpr int DCH = 1024;   // assignments per chunk
 constexpr int DMAXE = 1024; // max experts
-constexpr int DUN = 16;     // chunk histograms read per round in the scatter prologue
+constexpr int DUN = 32;     // chunk histograms read per round in the scatter prologue (all of them at 4096 tokens)
 
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ idx,
                                                          int64_t TK, int E,
