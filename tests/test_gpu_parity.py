@@ -232,6 +232,25 @@ def test_layer(name, overlap):
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
+def test_layer_equals_separate_calls(name):
+    """moe_layer gives bit for bit the y of its steps called one by one
+    (route, dispatch, expert GEMM, weighted combine): the layer's fusions
+    (top-k counting the dispatch histograms, GEMM-1 gathering x rows through
+    perm) change no value."""
+    import torch
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    y, r = M.layer(p, d["x"], d["w_gate"], d["bias"], d["w1"], d["w3"], d["w2"], routing=True)
+    idx, wt = M.route(p, d["x"], d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, d["x"])
+    h, yp = M.expert_gemm(p, o["x_packed"], o["offsets"], d["w1"], d["w3"], d["w2"])
+    ys = M.combine(p, yp, o["inv"], wt)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), host(r["topk_idx"]))
+    assert np.array_equal(host(ys), host(y)), "separate calls differ from moe_layer"
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
 def test_layer_fold_weight(name):
     """Routing weights folded into the down projection (MOE_F_FOLD_WEIGHT):
     routing and dispatch as the plain layer, y against the oracle's folded
