@@ -346,7 +346,7 @@ __device__ __forceinline__ void bd_tile(const bf16_t* __restrict__ A, const bf16
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acc[mt][t][r];
-        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a * sc;
+        o[r] = SWIGLU ? silu_mul(a, acc[mt][t + 4][r]) : a * sc;
       }
       if (row < R && col < N)
         *reinterpret_cast<u32x2*>(C + (int64_t)(r0 + row) * N + col) =

@@ -343,7 +343,7 @@ __device__ __forceinline__ void dt_block(const bf16_t* __restrict__ A, const bf1
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = acc[mt][t][r];
-        o[r] = SWIGLU ? a / (1.0f + expf(-a)) * acc[mt][t + 4][r] : a * sc;
+        o[r] = SWIGLU ? silu_mul(a, acc[mt][t + 4][r]) : a * sc;
       }
       *reinterpret_cast<u32x2*>(stg + i * RB + 32 * (t ^ (i & (NCH - 1))) + 8 * g) =
           u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};

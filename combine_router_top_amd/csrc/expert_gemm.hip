@@ -271,7 +271,7 @@ __device__ __forceinline__ void gemm_body(const bf16_t* __restrict__ A, const bf
           for (int r = 0; r < 4; ++r) {
             const float a = acc[mt][c][r];
             const float b = slot[((mt * CPL + c) * 4 + r) * 64];
-            acc[mt][c][r] = a / (1.0f + expf(-a)) * b;
+            acc[mt][c][r] = silu_mul(a, b);
           }
     }
   }
