@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--fold", action="store_true",
                     help="routing weights applied in the down projection (MOE_F_FOLD_WEIGHT)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="layer steps only (60 untimed, W warm-up, K timed, the expert GEMM timed "
+                         "inside each), for kernel traces whose per-kernel averages are the "
+                         "step's own launches; prints a reduced JSON object, not the bench line")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy that measures practical HBM bandwidth")
@@ -604,6 +608,28 @@ def main():
     counts = np.diff(offsets)
     A = int(offsets[-1])
     active = int((counts > 0).sum())
+
+    if a.steps_only:
+        for _ in range(60 + a.warmup):
+            step()
+        torch.cuda.synchronize()
+        gev = HipEvents(2 * a.steps) if not a.overlap else None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(a.steps):
+            if gev:
+                M.layer_set_gemm_events(gev.ev[2 * i], gev.ev[2 * i + 1])
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        gemm_us = None
+        if gev:
+            gemm_us = 1e3 * float(np.mean([gev.elapsed_ms(2 * i, 2 * i + 1) for i in range(a.steps)]))
+            gev.close()
+        print(json.dumps({"workload": w.name, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+                          "tokens_per_s": w.T / (ms * 1e-3), "expert_gemm_in_step_us": gemm_us}))
+        return
 
     # The untimed context figures run before the warm-up: the HBM ceilings,
     # then each ABI call on its own, cold (after a cache-evicting read) and
