@@ -250,6 +250,30 @@ def test_layer_equals_separate_calls(name):
     assert np.array_equal(host(ys), host(y)), "separate calls differ from moe_layer"
 
 
+@pytest.mark.parametrize("name", ["wide_dsv3_like", "medium_w512", "big_tails"])
+def test_expert_gemm_large_activations(name):
+    """x scaled by 64 (exact in bf16) so that GEMM-1's products reach a few
+    hundred in magnitude: the SiLU of every epilogue (thin, medium and large
+    tiles) passes through the range where e^-a overflows or underflows in
+    fp32, and h and y_packed still match the oracle within the bar."""
+    w, inp, ref, d = case(name)
+    p = M.Spec.of(w)
+    xs = d["x"] * 64
+    idx, wt = M.route(p, xs, d["w_gate"], d["bias"])
+    o = M.dispatch(p, idx, xs)
+    h, yp = M.expert_gemm(p, o["x_packed"], o["offsets"], d["w1"], d["w3"], d["w2"])
+    offsets = host(o["offsets"])
+    A = int(offsets[-1])
+    xp = host(o["x_packed"])[:A]
+    hr, ypr = O.swiglu_experts(xp, offsets, inp["w1"], inp["w3"], inp["w2"], w.dtype)
+    a1 = O.widen(xp, w.dtype).astype(np.float64) @ O.widen(inp["w1"][0], w.dtype).astype(np.float64)
+    assert np.abs(a1).max() > 100, "the scaled input should reach the exponential's saturation"
+    hg = O.widen(host(h)[:A], w.dtype)
+    assert np.all(np.isfinite(hg))
+    check_close(hg, hr, w.dtype, "h (large activations)")
+    check_close(O.widen(host(yp)[:A], w.dtype), ypr, w.dtype, "y_packed (large activations)")
+
+
 @pytest.mark.parametrize("name", ["wide_dsv3_like", "router_dma_tails", "big_mixed", "thin_tcols448",
                                   "fp32_mid"])
 def test_layer_graph_capture(name):
